@@ -1,0 +1,146 @@
+/*
+ * specverify.h - C ABI of libspecverify, the verify step of speculative
+ * sampling on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (the pages, cited by title and section):
+ *   [A] "Speculative Decoding: Cách LLM Sinh Văn Bản Nhanh Gấp 2–3 Lần" (anhtu.dev)
+ *   [B] "投机解码：让大模型「猜」着跑的数学魔术" (blog.oscine.io)
+ *   [C] "5.3 Medusa, EAGLE và MTP" (infra-guide-du8.pages.dev)
+ *   [D] "Спекулятивное декодирование: ускорение инференса LLM на 20–50%" (glukhov.org)
+ *
+ * Conventions shared by every entry point:
+ *  - Array arguments are DEVICE pointers owned by the caller; the library
+ *    never frees or retains them.  Layouts are row-major and contiguous with
+ *    the vocabulary innermost: logits_p [B][K+1][V], logits_q [B][K][V],
+ *    draft_tokens / u_accept [B][K], u_resample / out_n_accepted [B],
+ *    out_tokens [B][K+1].
+ *  - Logit element type: SPECV_F32 (float) or SPECV_BF16 (bfloat16 bits).
+ *    Pointers must be aligned to their element size; 16-byte alignment with
+ *    V*element_size a multiple of 16 selects the vectorised sweep, anything
+ *    else a scalar sweep with the same results.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    nothing synchronises: results are valid once the caller synchronises.
+ *    Argument checks happen on the host before any HIP call; a non-zero
+ *    return means nothing was enqueued (SPECV_E_HIP: a launch failed).
+ *  - No allocation: the caller passes a workspace of at least
+ *    spec_verify_workspace_size() bytes (256-byte aligned).  Concurrent calls
+ *    must use distinct workspaces.  Inputs are read-only; outputs are fully
+ *    overwritten.
+ *  - Logits must be finite or -inf with at least one finite value per row
+ *    (NaN gives unspecified tokens, never an out-of-bounds access).  A draft
+ *    id outside [0, V) fails its acceptance test and sets flag bit 2.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype_t;
+
+#define SPECV_OK            0
+#define SPECV_E_NULL       -1   /* a required pointer is NULL */
+#define SPECV_E_SHAPE      -2   /* B < 1, K < 1, K > SPECV_MAX_K, V < 1, or sizes overflow */
+#define SPECV_E_DTYPE      -3   /* dtype is not a specv_dtype_t */
+#define SPECV_E_TEMP       -4   /* T is NaN, infinite, negative, or so small that 1/T overflows */
+#define SPECV_E_WORKSPACE  -5   /* workspace NULL, misaligned, or smaller than required */
+#define SPECV_E_ALIGN      -6   /* a logits pointer is not aligned to its element size */
+#define SPECV_E_HIP        -7   /* a kernel launch failed */
+#define SPECV_E_ARG        -8   /* another argument is out of range (e.g. draw_policy) */
+
+#define SPECV_MAX_K        32   /* one 64-lane wave runs the acceptance scan */
+
+/* Draw policies of spec_verify_ex (test and diagnostic use). */
+#define SPECV_DRAW_CERTIFIED 0  /* fp32 draw, fp64 redo when its margin is below the error bound (default) */
+#define SPECV_DRAW_FP64      1  /* always redo the draw in fp64 */
+#define SPECV_DRAW_FP32      2  /* never redo: fp32 draw only (exposes the fast path's own accuracy) */
+
+/* Flag bits of out_flags. */
+#define SPECV_FLAG_REFINED   1  /* the draw was redone in fp64 */
+#define SPECV_FLAG_ZW_ZERO   2  /* residual mass was zero after rounding; drew from p_n instead */
+#define SPECV_FLAG_BAD_DRAFT 4  /* an evaluated draft id was outside [0, V) and was rejected */
+
+/*
+ * Bytes of workspace spec_verify needs for this shape.  Returns 0 when the
+ * shape or dtype is invalid.  T selects the mode: greedy (T == 0) needs less.
+ */
+size_t spec_verify_workspace_size(int B, int K, int V, int dtype, float T);
+
+/*
+ * spec_verify - one verify step for B sequences of K draft tokens.
+ *
+ * Sampling mode (T > 0).  With p_k = softmax(logits_p[b][k] / T) and
+ * q_k = softmax(logits_q[b][k] / T) ([A] "Toán học của sự miễn phí";
+ * [B] "拒绝采样"; [D] "Математическая гарантия"), draft token x_k =
+ * draft_tokens[b][k] is accepted iff u_accept[b][k] < min(1, p_k(x_k)/q_k(x_k))
+ * ([B] "验收标准的精确数学", equation alpha(x)), scanning k = 0, 1, ... and
+ * stopping at the first rejection n ([B] "多 Token 验证：左到右，遇错即停").
+ * At n < K the emitted token is drawn from max(0, p_n - q_n)/Z ([B]
+ * "拒绝之后怎么办？——残差分布", equations p_resid and Z; [D] equation r(x));
+ * at n == K it is drawn from p_K (the bonus token: [A] third rule of the
+ * acceptance procedure; [B] "多 Token 验证", fourth step).  The draw is an
+ * inverse CDF: the smallest token v, in ascending id order, whose running
+ * weight sum exceeds u_resample[b] times the total.
+ *
+ * Greedy mode (T == 0).  a_k = first index of the maximum of logits_p[b][k];
+ * accept while a_k == x_k; emit a_n ([C] section 9.1 greedy matching;
+ * [D] "Механизм «черновик — проверка»", longest matching prefix).
+ * logits_q, u_accept and u_resample are not read and may be NULL.
+ *
+ * Outputs: out_tokens[b] = x_0..x_{n-1}, the drawn token, then -1 padding;
+ * out_n_accepted[b] = n in [0, K] ([B] "多 Token 验证": one to k+1 tokens).
+ *
+ * logits_p      [B][K+1][V] target logits (dtype)
+ * logits_q      [B][K][V]   draft logits (dtype); may be NULL iff T == 0
+ * draft_tokens  [B][K] int32
+ * u_accept      [B][K] float in (0,1); may be NULL iff T == 0
+ * u_resample    [B]    float in (0,1); may be NULL iff T == 0
+ * T             temperature: 0 = greedy, else finite and > 0
+ * B, K, V       1 <= K <= SPECV_MAX_K, B >= 1, V >= 1
+ * out_tokens    [B][K+1] int32 (written)
+ * out_n_accepted[B] int32 (written)
+ * dtype         SPECV_F32 or SPECV_BF16
+ * workspace     device scratch of workspace_bytes >= spec_verify_workspace_size()
+ * stream        hipStream_t (as void*); NULL = null stream
+ * Returns SPECV_OK or a negative SPECV_E_* code.
+ */
+int spec_verify(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
+                const float* u_accept, const float* u_resample, float T, int B, int K, int V,
+                int32_t* out_tokens, int32_t* out_n_accepted, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_ex - spec_verify plus diagnostics for tests and benchmarks.
+ *
+ * out_logz    [B][2K+1] float or NULL: natural-log normalisers
+ *             log sum_v exp(logit/T), K+1 target rows then K draft rows
+ *             (sampling mode only; untouched when T == 0).
+ * out_flags   [B] int32 or NULL: SPECV_FLAG_* bits per sequence.
+ * draw_policy SPECV_DRAW_CERTIFIED (what spec_verify does), SPECV_DRAW_FP64
+ *             or SPECV_DRAW_FP32.
+ * ev_sweep_begin, ev_sweep_end
+ *             hipEvent_t (as void*) or NULL: when both are given they are
+ *             recorded on `stream` immediately before and after the row-sweep
+ *             kernel, so a caller can time that kernel alone.
+ */
+int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
+                   const float* u_accept, const float* u_resample, float T, int B, int K, int V,
+                   int32_t* out_tokens, int32_t* out_n_accepted, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream,
+                   float* out_logz, int32_t* out_flags, int draw_policy,
+                   void* ev_sweep_begin, void* ev_sweep_end);
+
+/* Static description of a return code. */
+const char* spec_verify_strerror(int code);
+
+/* Library version string, e.g. "libspecverify 0.1 gfx950". */
+const char* spec_verify_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECVERIFY_H */
