@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-sampling verify step on one MI355X.
+
+One step = one call of the whole verify path (row sweep, acceptance scan,
+draw, conditional fp64 refine) over one batch of the headline workload:
+B=256 sequences, K=8 drafts, V=128256, bf16 logits, T=0.7.  Inputs are
+generated on the host, copied to HBM once, and stay resident; the timed
+region is K back-to-back steps between two synchronisations.  The whole
+input (1.1 GB) exceeds the 256 MB Infinity Cache, so no step is served from
+a previous step's cache.
+
+Prints one JSON line.  `roofline` describes the dominant kernel (the row
+sweep), timed with HIP events recorded around it inside every timed step;
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published peak
+HEADLINE = 2
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "sweep_lse_headline_counters.md")
+SWEEP_SOURCE = os.path.join(ROOT, "speculative_sampling_verify_spec_amd", "csrc", "k_sweep.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t pairs from the HIP runtime torch already loaded."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0 and self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a.value, b.value))
+
+    def elapsed_ms(self, i: int) -> float:
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), *self.pairs[i]) == 0
+        return ms.value
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+
+
+def counter_traffic(swept_bytes: int):
+    """HBM bytes per sweep launch from the committed rocprofv3 counter summary,
+    or None when it is missing or was taken on a different sweep kernel."""
+    if not os.path.exists(COUNTER_SUMMARY):
+        return None
+    text = open(COUNTER_SUMMARY).read()
+    src = hashlib.sha256(open(SWEEP_SOURCE, "rb").read()).hexdigest()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.e+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src:
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(batch, gpu_tokens, gpu_n, budget_s: float):
+    """The fp64 oracle, as it stands, on the first sequences of the same batch
+    until about budget_s seconds of single-threaded work are spent."""
+    import numpy as np
+    from oracle import verify_batch
+    done, t0 = 0, time.perf_counter()
+    mismatched = 0
+    while done < batch.B and time.perf_counter() - t0 < budget_s:
+        r = verify_batch(batch, seqs=[done])
+        if r.n_accepted[0] != gpu_n[done] or not np.array_equal(r.tokens[0], gpu_tokens[done]):
+            mismatched += 1
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "verified seq-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of the {batch.B} sequences of the timed batch, fp64 numpy, one thread",
+            "seconds": round(dt, 2), "sample_mismatches_vs_gpu": mismatched}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=HEADLINE, choices=range(5))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verify step is data-parallel "
+              "over sequences and a multi-GPU run would shard B across processes", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verify_spec_amd as sv
+    import workloads
+
+    sv.load()
+    wl = workloads.WORKLOADS[args.workload]
+    log(f"generating {wl.name}: {wl.describe()}")
+    t0 = time.perf_counter()
+    batch = workloads.make_batch(args.workload, workers=workloads.default_workers())
+    log(f"generated in {time.perf_counter() - t0:.1f}s; copying to HBM")
+    lp, lq, x, ua, ur = workloads.to_device(batch)
+    B, K, V, T = batch.B, batch.K, batch.V, batch.T
+    greedy = T == 0.0
+    elt = 2 if batch.dtype == "bf16" else 4
+    dt_code = sv.SPECV_BF16 if batch.dtype == "bf16" else sv.SPECV_F32
+    ws = torch.empty(sv.workspace_size(B, K, V, dt_code, T), dtype=torch.uint8, device="cuda")
+    tokens = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
+    n_acc = torch.empty((B,), dtype=torch.int32, device="cuda")
+    flags = torch.empty((B,), dtype=torch.int32, device="cuda")
+    ev = HipEvents(args.steps)
+
+    def step(e=None):
+        rc = sv.spec_verify(lp, lq, x, ua, ur, T, tokens, n_acc, ws, out_flags=flags, events=e, extended=True)
+        if rc != 0:
+            raise RuntimeError(sv.strerror(rc))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warm; timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev.pairs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sweep_ms = [ev.elapsed_ms(i) for i in range(args.steps)]
+    ev.close()
+
+    n_host = n_acc.cpu().numpy()
+    tok_host = tokens.cpu().numpy()
+    refined = int(np.sum(flags.cpu().numpy() & sv.FLAG_REFINED))
+    rows_swept = B * (K + 1) if greedy else B * (2 * K + 1)
+    swept = rows_swept * V * elt
+    reread = 0 if greedy else int(np.sum(np.where(n_host < K, 2, 1))) * V * elt
+    step_s = wall / args.steps
+    sweep_s = float(np.mean(sweep_ms)) / 1e3
+    achieved = swept / sweep_s / 1e9
+    traffic = counter_traffic(swept)
+    line = {
+        "metric": "verified seq-steps/s + HBM GB/s (% peak), B=256 K=8 V=128256 bf16",
+        "value": B / step_s,
+        "unit": "verified seq-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: verify {wl.describe()}, logits {batch.dtype}",
+                   "B": B, "K": K, "V": V, "logits": batch.dtype, "T": T, "parallelism": "none (one GPU)"},
+        "hbm_gbps_algorithmic": (swept + reread) / step_s / 1e9,
+        "hbm_frac_of_peak": (swept + reread) / step_s / 1e9 / PEAK_HBM_GBS,
+        "bytes_per_step": {"swept": swept, "decisive_reread": reread},
+        "mean_accepted": float(np.mean(n_host)),
+        "refined_draws": refined,
+        "roofline": {"bound": "hbm", "kernel": "sweep_lse" if not greedy else "sweep_argmax",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "launch_us": sweep_s * 1e6, "algorithmic_bytes_per_launch": swept},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the fp64 oracle on a sample (~{args.cpu_seconds:.0f}s)")
+        line["cpu_baseline"] = cpu_baseline(batch, tok_host, n_host, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

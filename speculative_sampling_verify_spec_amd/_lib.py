@@ -1,0 +1,166 @@
+"""ctypes binding of libspecverify (argument marshalling only).
+
+Every step of the verify pass runs in the library's HIP kernels; this module
+checks shapes and dtypes, allocates outputs and the workspace with torch, and
+passes raw device pointers plus torch's current HIP stream.  There is no CPU
+fallback: a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libspecverify.so")
+
+SPECV_F32, SPECV_BF16 = 0, 1
+SPECV_MAX_K = 32
+DRAW_CERTIFIED, DRAW_FP64, DRAW_FP32 = 0, 1, 2
+FLAG_REFINED, FLAG_ZW_ZERO, FLAG_BAD_DRAFT = 1, 2, 4
+
+ERRORS = {0: "SPECV_OK", -1: "SPECV_E_NULL", -2: "SPECV_E_SHAPE", -3: "SPECV_E_DTYPE", -4: "SPECV_E_TEMP",
+          -5: "SPECV_E_WORKSPACE", -6: "SPECV_E_ALIGN", -7: "SPECV_E_HIP", -8: "SPECV_E_ARG"}
+
+# every symbol include/specverify.h declares
+EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_ex", "spec_verify_strerror",
+           "spec_verify_version")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the built library (raises FileNotFoundError if it was never built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    # torch first: its bundled HIP runtime carries the same soname, so the
+    # library binds to the one runtime instance torch's streams belong to
+    import torch  # noqa: F401
+    if not os.path.exists(p):
+        raise FileNotFoundError(f"{p} is missing: build it with `python -m speculative_sampling_verify_spec_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.spec_verify_workspace_size.argtypes = [i32, i32, i32, i32, f32]
+    lib.spec_verify_workspace_size.restype = sz
+    common = [vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, i32, vp, sz, vp]
+    lib.spec_verify.argtypes = common
+    lib.spec_verify.restype = i32
+    lib.spec_verify_ex.argtypes = common + [vp, vp, i32, vp, vp]
+    lib.spec_verify_ex.restype = i32
+    lib.spec_verify_strerror.argtypes = [i32]
+    lib.spec_verify_strerror.restype = ctypes.c_char_p
+    lib.spec_verify_version.argtypes = []
+    lib.spec_verify_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().spec_verify_strerror(code).decode()
+
+
+def version() -> str:
+    return load().spec_verify_version().decode()
+
+
+def workspace_size(B: int, K: int, V: int, dtype: int, T: float) -> int:
+    return int(load().spec_verify_workspace_size(B, K, V, dtype, T))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SPECV_BF16
+    if t.dtype == torch.float32:
+        return SPECV_F32
+    raise TypeError(f"logits must be torch.bfloat16 or torch.float32, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float,
+                out_tokens=None, out_n_accepted=None, workspace=None, *,
+                out_logz=None, out_flags=None, draw_policy: int = DRAW_CERTIFIED,
+                events=None, stream=None, extended: bool = False) -> int:
+    """Raw call with caller-provided device tensors; returns the library's status code."""
+    lib = load()
+    B, K1, V = logits_p.shape
+    K = K1 - 1
+    dt = _dtype_code(logits_p)
+    import torch
+    st = stream if stream is not None else torch.cuda.current_stream(logits_p.device).cuda_stream
+    args = [_ptr(logits_p), _ptr(logits_q), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resample),
+            float(T), B, K, V, _ptr(out_tokens), _ptr(out_n_accepted), dt,
+            _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(), st]
+    if not extended and out_logz is None and out_flags is None and draw_policy == DRAW_CERTIFIED and events is None:
+        return int(lib.spec_verify(*args))
+    e0, e1 = events if events is not None else (None, None)
+    return int(lib.spec_verify_ex(*args, _ptr(out_logz), _ptr(out_flags), draw_policy, e0, e1))
+
+
+def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
+           return_logz: bool = False, return_flags: bool = False, draw_policy: int = DRAW_CERTIFIED,
+           workspace=None, events=None):
+    """One verify step on torch device tensors.
+
+    logits_p [B,K+1,V] and logits_q [B,K,V] (bf16 or fp32, contiguous, same
+    device), draft_tokens [B,K] int32, u_accept [B,K] and u_resample [B]
+    float32; logits_q / u_accept / u_resample may be None when T == 0.
+    Returns (tokens [B,K+1] int32, n_accepted [B] int32) plus log Z
+    [B,2K+1] float32 and flags [B] int32 when asked.  Runs on torch's current
+    stream; nothing synchronises."""
+    import torch
+    dev = logits_p.device
+    if dev.type != "cuda":
+        raise ValueError("logits_p must be a device tensor")
+    if logits_p.dim() != 3:
+        raise ValueError("logits_p must be [B, K+1, V]")
+    B, K1, V = logits_p.shape
+    K = K1 - 1
+    greedy = float(T) == 0.0
+    tensors = [logits_p, draft_tokens] + ([] if greedy else [logits_q, u_accept, u_resample])
+    for t in tensors:
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("all inputs must be contiguous tensors on the same device")
+    if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, K):
+        raise ValueError("draft_tokens must be int32 [B, K]")
+    if not greedy:
+        if logits_q.dtype != logits_p.dtype or tuple(logits_q.shape) != (B, K, V):
+            raise ValueError("logits_q must match logits_p's dtype and be [B, K, V]")
+        if u_accept.dtype != torch.float32 or tuple(u_accept.shape) != (B, K):
+            raise ValueError("u_accept must be float32 [B, K]")
+        if u_resample.dtype != torch.float32 or tuple(u_resample.shape) != (B,):
+            raise ValueError("u_resample must be float32 [B]")
+    else:
+        logits_q = u_accept = u_resample = None
+    dt = _dtype_code(logits_p)
+    need = workspace_size(B, K, V, dt, float(T))
+    if need == 0:
+        raise SpecVerifyError(-2, "invalid shape, dtype or temperature")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    logz = torch.empty((B, 2 * K + 1), dtype=torch.float32, device=dev) if return_logz else None
+    flags = torch.empty((B,), dtype=torch.int32, device=dev) if return_flags else None
+    rc = spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T, tokens, n_acc, workspace,
+                     out_logz=logz, out_flags=flags, draw_policy=draw_policy, events=events)
+    if rc != 0:
+        raise SpecVerifyError(rc, strerror(rc))
+    out = (tokens, n_acc)
+    if return_logz:
+        out += (logz,)
+    if return_flags:
+        out += (flags,)
+    return out

@@ -1,0 +1,155 @@
+// Device-side helpers shared by the libspecverify kernels: element loads for
+// fp32 / bf16 rows, wave and workgroup reductions, and an fp64 block scan.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sv_internal.h"
+
+namespace sv {
+
+// ---------------------------------------------------------------- loads --
+// DT 0: fp32 logits; DT 1: bf16 logits (raw 16-bit patterns).
+template <int DT> struct Elt;
+
+template <> struct Elt<0> {
+  static constexpr int kPerVec = 4;  // elements per 16-byte vector
+  static constexpr int kBytes = 4;
+  __device__ static float at(const void* row, long i) { return static_cast<const float*>(row)[i]; }
+  __device__ static void unpack(const uint4& v, float* e) {
+    e[0] = __uint_as_float(v.x); e[1] = __uint_as_float(v.y);
+    e[2] = __uint_as_float(v.z); e[3] = __uint_as_float(v.w);
+  }
+};
+
+template <> struct Elt<1> {
+  static constexpr int kPerVec = 8;
+  static constexpr int kBytes = 2;
+  __device__ static float at(const void* row, long i) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(row)[i]) << 16);
+  }
+  // bf16 -> fp32 is exact: the 16 bits become the high half of the fp32 word.
+  __device__ static void unpack(const uint4& v, float* e) {
+    e[0] = __uint_as_float(v.x << 16); e[1] = __uint_as_float(v.x & 0xffff0000u);
+    e[2] = __uint_as_float(v.y << 16); e[3] = __uint_as_float(v.y & 0xffff0000u);
+    e[4] = __uint_as_float(v.z << 16); e[5] = __uint_as_float(v.z & 0xffff0000u);
+    e[6] = __uint_as_float(v.w << 16); e[7] = __uint_as_float(v.w & 0xffff0000u);
+  }
+};
+
+template <int DT>
+__device__ inline const void* row_ptr(const void* base, long row, int V) {
+  return static_cast<const char*>(base) + row * static_cast<long>(V) * Elt<DT>::kBytes;
+}
+
+__device__ inline uint4 load16(const void* row, long vec_index) {
+  return static_cast<const uint4*>(row)[vec_index];
+}
+
+// Raw hardware exp2 (v_exp_f32).  Arguments below -126 give 0 or a denormal;
+// callers only feed it values <= 0 whose tiny results do not matter.
+__device__ inline float ex2(float t) { return __builtin_amdgcn_exp2f(t); }
+
+// ----------------------------------------------------------- reductions --
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Combine (max, sum-scaled-to-max) pairs where sum = sum 2^((x - max) c).
+__device__ inline void lse_merge(float& m, float& s, float m2, float s2, float c) {
+  const float M = fmaxf(m, m2);
+  const float a = (m == -INFINITY) ? 0.f : s * ex2((m - M) * c);
+  const float b = (m2 == -INFINITY) ? 0.f : s2 * ex2((m2 - M) * c);
+  m = M;
+  s = a + b;
+}
+
+__device__ inline void wave_lse(float& m, float& s, float c) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, kWave);
+    const float s2 = __shfl_xor(s, o, kWave);
+    lse_merge(m, s, m2, s2, c);
+  }
+}
+
+// (value, index) arg-max merge: larger value wins, equal values keep the lower index.
+__device__ inline void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+__device__ inline void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(v, o, kWave);
+    const int i2 = __shfl_xor(i, o, kWave);
+    argmax_merge(v, i, v2, i2);
+  }
+}
+
+// Workgroup-wide sum of one double per thread; every thread gets the total.
+__device__ inline double block_sum(double v, double* lds /* >= kWaves */) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) lds[w] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) t += lds[i];
+  return t;
+}
+
+__device__ inline float block_max(float v, float* lds /* >= kWaves */) {
+  v = wave_max(v);
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) lds[w] = v;
+  __syncthreads();
+  float t = lds[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) t = fmaxf(t, lds[i]);
+  return t;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ inline double wave_inclusive_scan(double v) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Exclusive prefix sum of one double per thread over the workgroup, in
+// thread order.  Returns the exclusive prefix; *total gets the block total.
+__device__ inline double block_exclusive_scan(double v, double* lds /* >= kWaves */, double* total) {
+  const double inc = wave_inclusive_scan(v);
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  double excl = __shfl_up(inc, 1, kWave);
+  if (lane == 0) excl = 0.0;
+  __syncthreads();
+  if (lane == kWave - 1) lds[w] = inc;
+  __syncthreads();
+  double before = 0.0, all = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < w) before += lds[i];
+    all += lds[i];
+  }
+  *total = all;
+  return before + excl;
+}
+
+}  // namespace sv

@@ -1,0 +1,74 @@
+// Internal definitions shared by the libspecverify host code and kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kBlock = 256;   // threads per workgroup in every kernel
+constexpr int kWave = 64;     // CDNA wavefront width
+constexpr int kWaves = kBlock / kWave;
+constexpr int kMaxDrawChunks = 64;    // draw chunks per row: one wave combines them
+
+// Per-sequence record written by the acceptance scan and read by the draw.
+struct SeqRec {
+  int32_t n;       // accepted draft tokens
+  int32_t flags;   // SPECV_FLAG_* set so far
+  float mp, mq;    // maximum logit of the decisive target / draft row
+  double lp2, lq2; // log2 sum_v 2^((x_v - m) * c) of those rows (c = log2(e)/T in fp32)
+};
+static_assert(sizeof(SeqRec) == 32, "SeqRec layout");
+
+// Everything a kernel needs, passed by value.
+struct Params {
+  const void* lp;            // [B][K+1][V] target logits
+  const void* lq;            // [B][K][V] draft logits (sampling only)
+  const int32_t* x;          // [B][K] draft tokens
+  const float* ua;           // [B][K]
+  const float* ur;           // [B]
+  int B, K, V;
+  int vec;                   // 1: 16-byte vector loads are legal for every row
+  float c;                   // log2(e) / T rounded to fp32 (fast path)
+  double inv_t;              // 1 / T in fp64 (refine path)
+  int32_t* out_tokens;       // [B][K+1]
+  int32_t* out_n;            // [B]
+  float* out_logz;           // [B][2K+1] or null
+  int32_t* out_flags;        // [B] or null
+  int policy;                // SPECV_DRAW_*
+  double e_abs_res;          // certified bound, residual draws (probability-mass units)
+  double e_rel_bonus;        // certified bound, bonus draws (relative to the row's own sum)
+  // workspace
+  float2* part;              // [rows][nch1] (max, scaled sum) or (max, index bits) in greedy mode
+  SeqRec* rec;               // [B]
+  uint32_t* cnt_draw;        // [B] arrival counters of the draw chunks
+  uint32_t* cnt_ref;         // [B] arrival counters of the refine chunks
+  uint32_t* list_count;      // [1] number of sequences queued for the fp64 refine
+  int32_t* list;             // [B] their ids
+  double* csum;              // [B][R3] draw chunk sums
+  double2* rpart;            // [B][2][R4] refine (max, sum) partials
+  double2* rsum;             // [B][R4] refine chunk sums (residual, target)
+  int nch1, ch1;             // sweep chunks per row, elements per sweep chunk
+  int R3, ch3;               // draw chunks per row, elements per draw chunk
+  int R4, ch4;               // refine chunks per row, elements per refine chunk
+  int refine_grid;           // workgroups of each refine launch
+};
+
+// Workspace layout (byte offsets), shared by spec_verify_workspace_size and the launcher.
+struct Layout {
+  size_t part, rec, cnt, csum, list, rpart, rsum, total;
+  int nch1, ch1, R3, ch3, R4, ch4;
+};
+
+Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy);
+
+// Launchers (one per kernel), defined next to their kernels.
+hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_accept_scan(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_greedy_scan(const Params& p, hipStream_t s);
+hipError_t launch_draw(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_refine(const Params& p, int dtype, hipStream_t s);
+
+}  // namespace sv

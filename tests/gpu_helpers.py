@@ -1,0 +1,22 @@
+"""GPU-side helpers of the parity tests: run the HIP path on a batch."""
+import numpy as np
+
+import workloads
+from oracle.parity import GpuOut
+
+
+def run_gpu(sv, batch, policy=0, dev_inputs=None) -> GpuOut:
+    import torch
+    lp, lq, x, ua, ur = dev_inputs if dev_inputs is not None else workloads.to_device(batch)
+    greedy = batch.T == 0.0
+    out = sv.verify(lp, lq, x, ua, ur, batch.T, return_logz=not greedy, return_flags=True, draw_policy=policy)
+    torch.cuda.synchronize()
+    if greedy:
+        tok, n, flags = out
+        logz = None
+    else:
+        tok, n, logz, flags = out
+        logz = logz.cpu().numpy()
+    return GpuOut(tok.cpu().numpy(), n.cpu().numpy(), logz, flags.cpu().numpy())
+
+

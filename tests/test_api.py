@@ -1,0 +1,112 @@
+"""The C ABI without a GPU: the library loads, exports what include/specverify.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_sampling_verify_spec_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+F32, BF16 = sv.SPECV_F32, sv.SPECV_BF16
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sv.load()
+
+
+def test_header_declarations_are_all_exported(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(spec_verify\w*)\s*\(", text, re.M))
+    assert declared == set(sv.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict((k, int(v)) for k, v in re.findall(r"#define\s+(SPECV_\w+)\s+(-?\d+)", text))
+    assert consts["SPECV_MAX_K"] == sv.SPECV_MAX_K
+    assert consts["SPECV_DRAW_CERTIFIED"] == sv.DRAW_CERTIFIED
+    assert consts["SPECV_DRAW_FP64"] == sv.DRAW_FP64 and consts["SPECV_DRAW_FP32"] == sv.DRAW_FP32
+    assert consts["SPECV_FLAG_REFINED"] == sv.FLAG_REFINED
+    assert consts["SPECV_FLAG_ZW_ZERO"] == sv.FLAG_ZW_ZERO and consts["SPECV_FLAG_BAD_DRAFT"] == sv.FLAG_BAD_DRAFT
+    for code, name in sv.ERRORS.items():
+        assert consts.get(name, 0) == code, name
+
+
+def test_version_and_strerror(lib):
+    assert "gfx950" in sv.version()
+    for code in sv.ERRORS:
+        assert sv.strerror(code) != "unknown error"
+    assert sv.strerror(12345) == "unknown error"
+
+
+def test_workspace_size(lib):
+    a = sv.workspace_size(256, 8, 128256, BF16, 0.7)
+    assert a > 0 and a % 256 == 0
+    assert sv.workspace_size(256, 8, 128256, BF16, 0.0) > 0          # greedy
+    assert sv.workspace_size(256, 8, 128256, BF16, 0.0) < a          # needs less
+    for bad in [(0, 8, 100, BF16, 1.0), (4, 0, 100, BF16, 1.0), (4, 33, 100, BF16, 1.0), (4, 8, 0, BF16, 1.0),
+                (4, 8, 100, 7, 1.0), (4, 8, 100, BF16, -1.0), (4, 8, 100, BF16, float("nan")),
+                (4, 8, 100, BF16, float("inf")), (4, 8, 100, BF16, 1e-45)]:
+        assert sv.workspace_size(*bad) == 0, bad
+
+
+# Fake device addresses: every call below must fail on the host before it
+# could touch them.
+P, Q, X, UA, UR, OT, ON = (0x10000 * i for i in range(1, 8))
+WS = 0x7000000
+
+
+def _call(lib, **kw):
+    a = dict(lp=P, lq=Q, x=X, ua=UA, ur=UR, T=1.0, B=4, K=3, V=128, ot=OT, on=ON, dtype=F32,
+             ws=WS, wsb=1 << 30, stream=None, logz=None, flags=None, policy=0)
+    a.update(kw)
+    return lib.spec_verify_ex(a["lp"], a["lq"], a["x"], a["ua"], a["ur"], a["T"], a["B"], a["K"], a["V"],
+                              a["ot"], a["on"], a["dtype"], a["ws"], a["wsb"], a["stream"], a["logz"],
+                              a["flags"], a["policy"], None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -3), (dict(dtype=-1), -3),
+    (dict(T=-0.5), -4), (dict(T=float("nan")), -4), (dict(T=float("inf")), -4), (dict(T=1e-45), -4),
+    (dict(lp=None), -1), (dict(x=None), -1), (dict(ot=None), -1), (dict(on=None), -1),
+    (dict(lq=None), -1), (dict(ua=None), -1), (dict(ur=None), -1),
+    (dict(B=0), -2), (dict(K=0), -2), (dict(K=33), -2), (dict(V=0), -2), (dict(B=-3), -2),
+    (dict(B=1 << 30, V=1 << 30), -2),
+    (dict(policy=3), -8), (dict(policy=-1), -8),
+    (dict(lp=P + 2), -6), (dict(lq=Q + 1, dtype=BF16), -6),
+    (dict(ws=None), -5), (dict(ws=WS + 8), -5), (dict(wsb=1024), -5),
+])
+def test_host_side_errors(lib, kw, code):
+    assert _call(lib, **kw) == code
+
+
+def test_greedy_does_not_need_draft_inputs(lib):
+    # with T == 0 the draft logits and uniforms may be NULL: the call gets as
+    # far as the workspace check
+    assert _call(lib, T=0.0, lq=None, ua=None, ur=None, wsb=16) == -5
+
+
+def test_plain_entry_point_checks_too(lib):
+    rc = lib.spec_verify(P, Q, X, UA, UR, 1.0, 4, 3, 128, OT, ON, F32, WS, 16, None)
+    assert rc == -5
+    rc = lib.spec_verify(None, Q, X, UA, UR, 1.0, 4, 3, 128, OT, ON, F32, WS, 1 << 30, None)
+    assert rc == -1
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        sv.verify(torch.zeros(1, 2, 8), torch.zeros(1, 1, 8), torch.zeros(1, 1, dtype=torch.int32),
+                  torch.zeros(1, 1), torch.zeros(1), 1.0)
+
+
+def test_missing_library_raises(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        sv.load(str(tmp_path / "nope.so"))

@@ -34,6 +34,7 @@ Workload recipe (one reading of the pages' setting, stated here in full):
 from __future__ import annotations
 
 import dataclasses
+import multiprocessing
 import os
 from concurrent.futures import ProcessPoolExecutor
 from typing import Iterable, Optional, Sequence
@@ -229,7 +230,8 @@ def make_batch(cfg_id: int, seqs: Optional[Iterable[int]] = None, seed: int = DE
     Kk = wl.K if K is None else K
     if workers > 1 and len(seqs) > 1:
         parts = np.array_split(seqs, min(workers * 4, len(seqs)))
-        with ProcessPoolExecutor(workers) as ex:
+        # forkserver: workers never fork a process that may hold a GPU context
+        with ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("forkserver")) as ex:
             out = [s for blk in ex.map(_gen_block, [(wl, cfg_id, p, seed, Vv, Kk) for p in parts]) for s in blk]
     else:
         out = _gen_block((wl, cfg_id, seqs, seed, Vv, Kk))
@@ -256,3 +258,23 @@ def custom_batch(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: floa
                  draft_tokens=np.asarray(draft_tokens, dtype=np.int32).reshape(B, K1 - 1),
                  u_accept=None if u_accept is None else np.asarray(u_accept, dtype=np.float32).reshape(B, K1 - 1),
                  u_resample=None if u_resample is None else np.asarray(u_resample, dtype=np.float32).reshape(B))
+
+
+def to_device(batch: Batch, device="cuda"):
+    """Copy a batch to torch device tensors (bf16 bit patterns become bfloat16)."""
+    import torch
+
+    def t(a, dt=None):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if dt is not None:
+            a = a.view(dt)
+        return torch.from_numpy(a).to(device)
+
+    if batch.dtype == "bf16":
+        lp = t(batch.logits_p, np.int16).view(torch.bfloat16)
+        lq = None if batch.logits_q is None else t(batch.logits_q, np.int16).view(torch.bfloat16)
+    else:
+        lp, lq = t(batch.logits_p), t(batch.logits_q)
+    return lp, lq, t(batch.draft_tokens.astype(np.int32)), t(batch.u_accept), t(batch.u_resample)
