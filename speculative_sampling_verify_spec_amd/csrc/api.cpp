@@ -17,30 +17,38 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int elt_bytes(int dtype) { return dtype == SPECV_BF16 ? 2 : 4; }
 
-// Error model of the fp32 draw, in units of u = 2^-24.  Per element the fast
-// path rounds (x - m) (exact for bf16), the product with c = log2(e)/T (c is
-// itself rounded), the subtraction of the fp32 log2 normaliser, and v_exp_f32
-// (taken as <= 2 ulp).  Weighted by p, these relative errors sum to a few
-// u * ln V: the p-weighted mean of |(x - m) c| and the log2 normaliser are
-// both at most log2 V.  The sweep's sums add their rounding (a tree of 8, four
-// adds, eight pair merges, each merge with one v_exp_f32).  row_error bounds
-// the error of any prefix mass of one normalised row.
+// Error model of the fp32 draw, in units of u = 2^-24.  The sweep forms
+// t = fma(x, c, -R) with R = rint(row-share max * c), so t <= 1/2 and its one
+// rounding is at most u|t|; v_exp_f32 is taken as <= 2 ulp; lane sums add a
+// tree of 8 and six adds; merges are exact power-of-two rescales in fp64.
+// The draw forms log2 p = fma(x, c, -whole) - fraction (two roundings of
+// size u |log2 p| + u/2) and a v_exp_f32.  c = log2(e)/T is itself rounded,
+// which acts as a relative temperature change of at most u.  Weighted by p,
+// |log2 p| averages at most log2 V, so each normalised row's prefix masses
+// carry a relative error of at most u (7 ln V + 12) + 2 exp errors.
 double row_error(int V) {
   const double u = std::ldexp(1.0, -24);
-  return u * (9.0 * std::log(static_cast<double>(V)) + 63.0);
+  return u * (7.0 * std::log(static_cast<double>(V)) + 12.0 + 8.0);
 }
 
 }  // namespace
 
 Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
   Layout L{};
-  const int per_vec = dtype == SPECV_BF16 ? 8 : 4;
-  L.ch1 = vec ? kBlock * 4 * per_vec : kBlock * 16;
-  L.nch1 = static_cast<int>((static_cast<long>(V) + L.ch1 - 1) / L.ch1);
+  // sweep chunks: equal shares of a row, each at most one workgroup's worth
+  const int per_vec = vec ? (dtype == SPECV_BF16 ? 8 : 4) : 1;
+  const int lane_elems = vec ? (dtype == SPECV_BF16 ? kSweepElems<1, true>() : kSweepElems<0, true>())
+                             : kSweepElems<0, false>();
+  L.ch1 = kBlock * lane_elems;  // elements per chunk, at most
+  const long units = static_cast<long>(V) / per_vec;
+  const long units_per_chunk = static_cast<long>(kBlock) * (lane_elems / per_vec);
+  L.nch1 = static_cast<int>((units + units_per_chunk - 1) / units_per_chunk);
+  L.cq = static_cast<int>(units / L.nch1);
+  L.cr = static_cast<int>(units % L.nch1);
   const long rows = static_cast<long>(B) * (greedy ? K + 1 : 2 * K + 1);
   size_t off = 0;
   L.part = off;
-  off = align_up(off + static_cast<size_t>(rows) * L.nch1 * sizeof(float2));
+  off = align_up(off + static_cast<size_t>(rows) * L.nch1 * kWaves * sizeof(float2));
   if (greedy) {
     L.total = off;
     return L;
@@ -54,7 +62,7 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
   L.rec = off;
   off = align_up(off + static_cast<size_t>(B) * sizeof(SeqRec));
   L.cnt = off;
-  off = align_up(off + (2 * static_cast<size_t>(B) + 1) * sizeof(uint32_t));
+  off = align_up(off + sizeof(uint32_t));
   L.csum = off;
   off = align_up(off + static_cast<size_t>(B) * L.R3 * sizeof(double));
   L.list = off;
@@ -143,6 +151,8 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   P.part = reinterpret_cast<float2*>(ws + L.part);
   P.nch1 = L.nch1;
   P.ch1 = L.ch1;
+  P.cq = L.cq;
+  P.cr = L.cr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = static_cast<hipEvent_t>(ev_sweep_begin), e1 = static_cast<hipEvent_t>(ev_sweep_end);
   const bool timed = e0 && e1;
@@ -165,9 +175,7 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   // bonus draw: only per-element rounding and the chunk sums remain (normaliser cancels)
   P.e_rel_bonus = 2.0 * 2.0 * u * (3.0 * lnV + 21.0);
   P.rec = reinterpret_cast<SeqRec*>(ws + L.rec);
-  P.cnt_draw = reinterpret_cast<uint32_t*>(ws + L.cnt);
-  P.cnt_ref = P.cnt_draw + B;
-  P.list_count = P.cnt_ref + B;
+  P.list_count = reinterpret_cast<uint32_t*>(ws + L.cnt);
   P.csum = reinterpret_cast<double*>(ws + L.csum);
   P.list = reinterpret_cast<int32_t*>(ws + L.list);
   P.rpart = reinterpret_cast<double2*>(ws + L.rpart);

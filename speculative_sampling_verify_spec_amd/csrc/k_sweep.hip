@@ -1,170 +1,140 @@
 // Row sweeps: the one pass over every logit that the verify step needs.
 //
-// Sampling mode: each workgroup reduces one chunk of one row to a pair
-// (m, s) with m the chunk's largest logit and s = sum 2^((x - m) * c),
-// c = log2(e) / T.  The normalisers log Z = m/T + ln(s) of the target and
-// draft distributions p and q are combined from these pairs afterwards.
-// Greedy mode: each workgroup reduces a chunk to (largest logit, lowest
-// index holding it).
+// Sampling mode: each wave reduces its share of one chunk of one row to a
+// pair (R, s): R a whole number (stored as float) and s = sum 2^(x*c - R),
+// c = log2(e) / T, so the share's sum of 2^(x*c) is s * 2^R.  The normalisers
+// log2 Z of the target and draft distributions p and q are combined from
+// these pairs afterwards with exact power-of-two rescales.
+// Greedy mode: each wave reduces its share of a chunk to (largest logit,
+// lowest index holding it).
 //
-// Memory: rows are read once, 16 bytes per lane per load when every row is
-// 16-byte aligned (4 fp32 or 8 bf16 values), coalesced across the wave; a
-// lane issues all its loads before it computes.  HBM-bound by design: about
-// six VALU operations and one v_exp_f32 per element against 2 or 4 bytes.
+// Per element the sampling sweep spends one bf16 widen (exact), half a
+// v_max3_f32, one fma t = x*c - R (R = rint(max * c), so t <= 0.5 and the
+// fma's single rounding is the only error in the exponent), one v_exp_f32 and
+// one add; the greedy sweep a widen and a compare-select.  Both are HBM-bound:
+// every row is read once with 16-byte non-temporal loads (4 fp32 or 8 bf16
+// values per lane, coalesced across the wave), all of a lane's loads issued
+// before it computes.  A row is split into chunks of equal size, one
+// workgroup each, so no workgroup gets a short tail; each wave writes its own
+// partial, so no workgroup barrier holds finished waves back.
 #include "sv_device.h"
 
 namespace sv {
 
 namespace {
 
-constexpr int kVecIters = 4;      // 16-byte loads per lane per chunk
-constexpr int kScalarIters = 16;  // scalar loads per lane per chunk
-
-// Zero the per-call arrival counters that the draw and refine kernels use.
-// Runs in the first kernel of a call, so stream order makes the zeros visible.
-__device__ inline void zero_counters(const Params& p) {
-  const long z = static_cast<long>(blockIdx.x) * kBlock + threadIdx.x;
-  if (z < p.B) {
-    p.cnt_draw[z] = 0u;
-    p.cnt_ref[z] = 0u;
-  }
-  if (z == 0) p.list_count[0] = 0u;
+// Reset the refine queue.  The first kernel of a call does it, so stream
+// order makes the zero visible to the draw that appends to the queue.
+__device__ inline void reset_queue(const Params& p) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.list_count[0] = 0u;
 }
 
-// Row `row` of the sampling sweep: K+1 target rows then K draft rows per sequence.
+// Row `row` of the sampling sweep: K+1 target rows then K draft rows per
+// sequence.  32-bit division: row counts are checked on the host.
 template <int DT>
-__device__ inline const void* sweep_row(const Params& p, long row) {
-  const int per_seq = 2 * p.K + 1;
-  const long s = row / per_seq;
-  const int j = static_cast<int>(row % per_seq);
-  return j <= p.K ? row_ptr<DT>(p.lp, s * (p.K + 1) + j, p.V)
-                  : row_ptr<DT>(p.lq, s * p.K + (j - p.K - 1), p.V);
+__device__ inline const void* sweep_row(const Params& p, uint32_t row) {
+  const uint32_t per_seq = 2u * p.K + 1u;
+  const uint32_t s = row / per_seq;
+  const uint32_t j = row - s * per_seq;
+  return j <= static_cast<uint32_t>(p.K) ? row_ptr<DT>(p.lp, static_cast<long>(s) * (p.K + 1) + j, p.V)
+                                         : row_ptr<DT>(p.lq, static_cast<long>(s) * p.K + (j - p.K - 1), p.V);
+}
+
+// This lane's elements of chunk `chunk` of a row (units of 16 bytes when VEC,
+// single elements otherwise), loaded without branches; elements past the
+// chunk read as -inf.  Returns the chunk's unit range.
+template <int DT, bool VEC>
+__device__ inline void load_chunk(const Params& p, const void* r, uint32_t chunk, float (&e)[kSweepElems<DT, VEC>()],
+                                  long& lo, long& hi) {
+  constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
+  constexpr int IT = kSweepElems<DT, VEC>() / PV;
+  lo = static_cast<long>(chunk) * p.cq + min(static_cast<int>(chunk), p.cr);
+  hi = lo + p.cq + (static_cast<int>(chunk) < p.cr ? 1 : 0);
+  if constexpr (VEC) {
+    uint4 raw[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const long u = lo + threadIdx.x + static_cast<long>(i) * kBlock;
+      raw[i] = load16_nt(r, u < hi ? u : hi - 1);
+    }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      Elt<DT>::unpack(raw[i], &e[i * PV]);
+      if (lo + threadIdx.x + static_cast<long>(i) * kBlock >= hi) {
+#pragma unroll
+        for (int k = 0; k < PV; ++k) e[i * PV + k] = -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) e[i] = load_masked<DT>(r, lo + threadIdx.x + static_cast<long>(i) * kBlock, hi);
+  }
 }
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
-  zero_counters(p);
-  const long row = blockIdx.x / p.nch1;
-  const int chunk = blockIdx.x % p.nch1;
-  const void* r = sweep_row<DT>(p, row);
+  reset_queue(p);
+  constexpr int N = kSweepElems<DT, VEC>();
+  constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
+  const uint32_t row = blockIdx.x / static_cast<uint32_t>(p.nch1);
+  const uint32_t chunk = blockIdx.x - row * static_cast<uint32_t>(p.nch1);
   const float c = p.c;
-  float m = -INFINITY, s = 0.f;
+  float e[N];
+  long lo, hi;
+  load_chunk<DT, VEC>(p, sweep_row<DT>(p, row), chunk, e, lo, hi);
 
-  if constexpr (VEC) {
-    constexpr int PV = Elt<DT>::kPerVec;
-    const long nvec = p.V / PV;
-    const long v0 = static_cast<long>(chunk) * (kBlock * kVecIters) + threadIdx.x;
-    float e[kVecIters][PV];
+  float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kVecIters; ++i) {
-      const long vi = v0 + static_cast<long>(i) * kBlock;
-      if (vi < nvec) {
-        Elt<DT>::unpack(load16(r, vi), e[i]);
-      } else {
+  for (int k = 0; k < N; ++k) m = fmaxf(m, e[k]);
+  float R = -INFINITY, s = 0.f;
+  if (m != -INFINITY) {
+    R = rintf(m * c);
 #pragma unroll
-        for (int k = 0; k < PV; ++k) e[i][k] = -INFINITY;
-      }
-    }
+    for (int i = 0; i < N / PV; ++i) {
+      float t[PV];
 #pragma unroll
-    for (int i = 0; i < kVecIters; ++i)
+      for (int k = 0; k < PV; ++k) t[k] = ex2(fmaf(e[i * PV + k], c, -R));
+      // pairwise within a 16-byte unit, then one add into the running sum
 #pragma unroll
-      for (int k = 0; k < PV; ++k) m = fmaxf(m, e[i][k]);
-    if (m != -INFINITY) {
+      for (int w = PV / 2; w > 0; w >>= 1)
 #pragma unroll
-      for (int i = 0; i < kVecIters; ++i) {
-        float t[PV];
-#pragma unroll
-        for (int k = 0; k < PV; ++k) t[k] = ex2((e[i][k] - m) * c);
-        // pairwise within the vector, then one add into the running sum
-#pragma unroll
-        for (int w = PV / 2; w > 0; w >>= 1)
-#pragma unroll
-          for (int k = 0; k < w; ++k) t[k] += t[k + w];
-        s += t[0];
-      }
-    }
-  } else {
-    const long e0 = static_cast<long>(chunk) * (kBlock * kScalarIters) + threadIdx.x;
-    float e[kScalarIters];
-#pragma unroll
-    for (int i = 0; i < kScalarIters; ++i) {
-      const long idx = e0 + static_cast<long>(i) * kBlock;
-      e[i] = idx < p.V ? Elt<DT>::at(r, idx) : -INFINITY;
-    }
-#pragma unroll
-    for (int i = 0; i < kScalarIters; ++i) m = fmaxf(m, e[i]);
-    if (m != -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < kScalarIters; i += 4)
-        s += (ex2((e[i] - m) * c) + ex2((e[i + 1] - m) * c)) + (ex2((e[i + 2] - m) * c) + ex2((e[i + 3] - m) * c));
+        for (int k = 0; k < w; ++k) t[k] += t[k + w];
+      s += t[0];
     }
   }
 
-  wave_lse(m, s, c);
-  __shared__ float lm[kWaves], ls[kWaves];
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  if (lane == 0) { lm[w] = m; ls[w] = s; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = lm[0], S = ls[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) lse_merge(M, S, lm[i], ls[i], c);
-    p.part[row * p.nch1 + chunk] = make_float2(M, S);
-  }
+  // wave merge: exact power-of-two rescale to the wave's largest R, fp64 sum
+  const float M = wave_max(R);
+  const double sd = (R == -INFINITY) ? 0.0 : static_cast<double>(ldexpf(s, static_cast<int>(fmaxf(R - M, -200.f))));
+  const double S = wave_sum(sd);
+  if (threadIdx.x % kWave == 0)
+    p.part[(static_cast<long>(row) * p.nch1 + chunk) * kWaves + threadIdx.x / kWave] = make_float2(M, static_cast<float>(S));
 }
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
-  const long row = blockIdx.x / p.nch1;  // target rows only: row = s * (K+1) + k
-  const int chunk = blockIdx.x % p.nch1;
-  const void* r = row_ptr<DT>(p.lp, row, p.V);
+  constexpr int N = kSweepElems<DT, VEC>();
+  constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
+  const uint32_t row = blockIdx.x / static_cast<uint32_t>(p.nch1);  // target rows only: s * (K+1) + k
+  const uint32_t chunk = blockIdx.x - row * static_cast<uint32_t>(p.nch1);
+  float e[N];
+  long lo, hi;
+  load_chunk<DT, VEC>(p, row_ptr<DT>(p.lp, row, p.V), chunk, e, lo, hi);
+  // a lane visits its elements in increasing index order, so a strict
+  // comparison keeps the lowest index among equal values
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-
-  if constexpr (VEC) {
-    constexpr int PV = Elt<DT>::kPerVec;
-    const long nvec = p.V / PV;
-    const long v0 = static_cast<long>(chunk) * (kBlock * kVecIters) + threadIdx.x;
-    uint4 raw[kVecIters];
 #pragma unroll
-    for (int i = 0; i < kVecIters; ++i) {
-      const long vi = v0 + static_cast<long>(i) * kBlock;
-      if (vi < nvec) raw[i] = load16(r, vi);
-    }
-    // a lane visits its elements in increasing index order, so a strict
-    // comparison keeps the lowest index among equal values
+  for (int i = 0; i < N / PV; ++i) {
+    const long u = lo + threadIdx.x + static_cast<long>(i) * kBlock;
+    if (u < hi) {
 #pragma unroll
-    for (int i = 0; i < kVecIters; ++i) {
-      const long vi = v0 + static_cast<long>(i) * kBlock;
-      if (vi < nvec) {
-        float e[PV];
-        Elt<DT>::unpack(raw[i], e);
-#pragma unroll
-        for (int k = 0; k < PV; ++k) argmax_merge(bv, bi, e[k], static_cast<int>(vi * PV + k));
-      }
-    }
-  } else {
-    const long e0 = static_cast<long>(chunk) * (kBlock * kScalarIters) + threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < kScalarIters; ++i) {
-      const long idx = e0 + static_cast<long>(i) * kBlock;
-      if (idx < p.V) argmax_merge(bv, bi, Elt<DT>::at(r, idx), static_cast<int>(idx));
+      for (int k = 0; k < PV; ++k) argmax_merge(bv, bi, e[i * PV + k], static_cast<int>(u * PV + k));
     }
   }
-
   wave_argmax(bv, bi);
-  __shared__ float lv[kWaves];
-  __shared__ int li[kWaves];
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  if (lane == 0) { lv[w] = bv; li[w] = bi; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float V0 = lv[0];
-    int I0 = li[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) argmax_merge(V0, I0, lv[i], li[i]);
-    p.part[row * p.nch1 + chunk] = make_float2(V0, __int_as_float(I0));
-  }
+  if (threadIdx.x % kWave == 0)
+    p.part[(static_cast<long>(row) * p.nch1 + chunk) * kWaves + threadIdx.x / kWave] = make_float2(bv, __int_as_float(bi));
 }
 
 }  // namespace

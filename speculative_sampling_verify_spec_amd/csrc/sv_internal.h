@@ -12,12 +12,22 @@ constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kWaves = kBlock / kWave;
 constexpr int kMaxDrawChunks = 64;    // draw chunks per row: one wave combines them
 
+// Elements one lane of the row sweep holds: six 16-byte units on the vector
+// path, sixteen single elements on the scalar path.
+template <int DT, bool VEC>
+constexpr int kSweepElems() {
+  return VEC ? 6 * (DT == 1 ? 8 : 4) : 16;
+}
+
 // Per-sequence record written by the acceptance scan and read by the draw.
+// A row's log2 normaliser log2 sum_v 2^(x_v * c) (c = log2(e)/T in fp32) is
+// stored as a whole number plus a fraction in [-1/2, 1/2], so the draw forms
+// log2 p(v) = fma(x_v, c, -whole) - fraction with a single large rounding.
 struct SeqRec {
   int32_t n;       // accepted draft tokens
   int32_t flags;   // SPECV_FLAG_* set so far
-  float mp, mq;    // maximum logit of the decisive target / draft row
-  double lp2, lq2; // log2 sum_v 2^((x_v - m) * c) of those rows (c = log2(e)/T in fp32)
+  float mp, mq;    // whole parts of the decisive target / draft row's log2 normaliser
+  double lp2, lq2; // their fractional parts
 };
 static_assert(sizeof(SeqRec) == 32, "SeqRec layout");
 
@@ -40,16 +50,15 @@ struct Params {
   double e_abs_res;          // certified bound, residual draws (probability-mass units)
   double e_rel_bonus;        // certified bound, bonus draws (relative to the row's own sum)
   // workspace
-  float2* part;              // [rows][nch1] (max, scaled sum) or (max, index bits) in greedy mode
+  float2* part;              // [rows][nch1][kWaves] (R, s) sweep partials, or (max, index bits) in greedy mode
   SeqRec* rec;               // [B]
-  uint32_t* cnt_draw;        // [B] arrival counters of the draw chunks
-  uint32_t* cnt_ref;         // [B] arrival counters of the refine chunks
   uint32_t* list_count;      // [1] number of sequences queued for the fp64 refine
   int32_t* list;             // [B] their ids
   double* csum;              // [B][R3] draw chunk sums
   double2* rpart;            // [B][2][R4] refine (max, sum) partials
   double2* rsum;             // [B][R4] refine chunk sums (residual, target)
-  int nch1, ch1;             // sweep chunks per row, elements per sweep chunk
+  int nch1, ch1;             // sweep chunks per row, elements per sweep chunk (at most)
+  int cq, cr;                // sweep chunk c spans c*cq + min(c, cr) .. + cq + (c < cr) units
   int R3, ch3;               // draw chunks per row, elements per draw chunk
   int R4, ch4;               // refine chunks per row, elements per refine chunk
   int refine_grid;           // workgroups of each refine launch
@@ -58,7 +67,7 @@ struct Params {
 // Workspace layout (byte offsets), shared by spec_verify_workspace_size and the launcher.
 struct Layout {
   size_t part, rec, cnt, csum, list, rpart, rsum, total;
-  int nch1, ch1, R3, ch3, R4, ch4;
+  int nch1, ch1, cq, cr, R3, ch3, R4, ch4;
 };
 
 Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy);

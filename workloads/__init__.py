@@ -29,14 +29,14 @@ Workload recipe (one reading of the pages' setting, stated here in full):
   (24 significant bits) and strictly inside (0, 1).
 * Seeds: sequence ``b`` of workload ``c`` draws from
   ``SeedSequence(entropy=[seed, c], spawn_key=(b,))`` in a fixed order, so any
-  subset of sequences can be regenerated alone, in any order, in parallel.
+  subset of sequences can be regenerated alone, in any order, in parallel
+  (threads).
 """
 from __future__ import annotations
 
 import dataclasses
-import multiprocessing
 import os
-from concurrent.futures import ProcessPoolExecutor
+from concurrent.futures import ThreadPoolExecutor
 from typing import Iterable, Optional, Sequence
 
 import numpy as np
@@ -230,8 +230,9 @@ def make_batch(cfg_id: int, seqs: Optional[Iterable[int]] = None, seed: int = DE
     Kk = wl.K if K is None else K
     if workers > 1 and len(seqs) > 1:
         parts = np.array_split(seqs, min(workers * 4, len(seqs)))
-        # forkserver: workers never fork a process that may hold a GPU context
-        with ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("forkserver")) as ex:
+        # threads, not processes: numpy's bulk generators release the GIL, and no
+        # child process is ever forked from a process that may hold a GPU context
+        with ThreadPoolExecutor(workers) as ex:
             out = [s for blk in ex.map(_gen_block, [(wl, cfg_id, p, seed, Vv, Kk) for p in parts]) for s in blk]
     else:
         out = _gen_block((wl, cfg_id, seqs, seed, Vv, Kk))
