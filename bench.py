@@ -154,7 +154,6 @@ def main():
 
     n_host = n_acc.cpu().numpy()
     tok_host = tokens.cpu().numpy()
-    refined = int(np.sum(flags.cpu().numpy() & sv.FLAG_REFINED))
     rows_swept = B * (K + 1) if greedy else B * (2 * K + 1)
     swept = rows_swept * V * elt
     reread = 0 if greedy else int(np.sum(np.where(n_host < K, 2, 1))) * V * elt
@@ -176,7 +175,6 @@ def main():
         "hbm_frac_of_peak": (swept + reread) / step_s / 1e9 / PEAK_HBM_GBS,
         "bytes_per_step": {"swept": swept, "decisive_reread": reread},
         "mean_accepted": float(np.mean(n_host)),
-        "refined_draws": refined,
         "roofline": {"bound": "hbm", "kernel": "sweep_lse" if not greedy else "sweep_argmax",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,

@@ -50,17 +50,10 @@ typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype_t;
 #define SPECV_E_WORKSPACE  -5   /* workspace NULL, misaligned, or smaller than required */
 #define SPECV_E_ALIGN      -6   /* a logits pointer is not aligned to its element size */
 #define SPECV_E_HIP        -7   /* a kernel launch failed */
-#define SPECV_E_ARG        -8   /* another argument is out of range (e.g. draw_policy) */
 
 #define SPECV_MAX_K        32   /* one 64-lane wave runs the acceptance scan */
 
-/* Draw policies of spec_verify_ex (test and diagnostic use). */
-#define SPECV_DRAW_CERTIFIED 0  /* fp32 draw, fp64 redo when its margin is below the error bound (default) */
-#define SPECV_DRAW_FP64      1  /* always redo the draw in fp64 */
-#define SPECV_DRAW_FP32      2  /* never redo: fp32 draw only (exposes the fast path's own accuracy) */
-
-/* Flag bits of out_flags. */
-#define SPECV_FLAG_REFINED   1  /* the draw was redone in fp64 */
+/* Flag bits of out_flags (bit 0 is unused). */
 #define SPECV_FLAG_ZW_ZERO   2  /* residual mass was zero after rounding; drew from p_n instead */
 #define SPECV_FLAG_BAD_DRAFT 4  /* an evaluated draft id was outside [0, V) and was rejected */
 
@@ -120,19 +113,16 @@ int spec_verify(const void* logits_p, const void* logits_q, const int32_t* draft
  *             log sum_v exp(logit/T), K+1 target rows then K draft rows
  *             (sampling mode only; untouched when T == 0).
  * out_flags   [B] int32 or NULL: SPECV_FLAG_* bits per sequence.
- * draw_policy SPECV_DRAW_CERTIFIED (what spec_verify does), SPECV_DRAW_FP64
- *             or SPECV_DRAW_FP32.
  * ev_sweep_begin, ev_sweep_end
  *             hipEvent_t (as void*) or NULL: when both are given they are
- *             recorded on `stream` immediately before and after the row-sweep
- *             kernel, so a caller can time that kernel alone.
+ *             recorded with the first and the last row-sweep dispatch of the
+ *             call, so a caller can time the row sweep alone.
  */
 int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
                    const float* u_accept, const float* u_resample, float T, int B, int K, int V,
                    int32_t* out_tokens, int32_t* out_n_accepted, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream,
-                   float* out_logz, int32_t* out_flags, int draw_policy,
-                   void* ev_sweep_begin, void* ev_sweep_end);
+                   float* out_logz, int32_t* out_flags, void* ev_sweep_begin, void* ev_sweep_end);
 
 /* Static description of a return code. */
 const char* spec_verify_strerror(int code);

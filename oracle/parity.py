@@ -39,7 +39,6 @@ class Report:
     excused: int
     failures: list
     max_logz_err: float
-    refined: int
 
     def check(self):
         assert not self.failures, f"{len(self.failures)} non-excused mismatches, first: {self.failures[:3]}"
@@ -92,5 +91,4 @@ def compare(batch, gpu: GpuOut, ref: oracle.Result, rows: np.ndarray | None = No
             else:
                 failures.append((int(b), "draw", j, int(ot[on]), dist))
     decisions = int(np.sum(np.minimum(ref.n_accepted + 1, K)) + len(rows))
-    refined = int(np.sum((gpu.flags[rows] & 1) != 0))
-    return Report(len(rows), decisions, excused, failures, max_lz, refined)
+    return Report(len(rows), decisions, excused, failures, max_lz)

@@ -16,11 +16,10 @@ LIB_PATH = os.path.join(PKG, "libspecverify.so")
 
 SPECV_F32, SPECV_BF16 = 0, 1
 SPECV_MAX_K = 32
-DRAW_CERTIFIED, DRAW_FP64, DRAW_FP32 = 0, 1, 2
-FLAG_REFINED, FLAG_ZW_ZERO, FLAG_BAD_DRAFT = 1, 2, 4
+FLAG_ZW_ZERO, FLAG_BAD_DRAFT = 2, 4
 
 ERRORS = {0: "SPECV_OK", -1: "SPECV_E_NULL", -2: "SPECV_E_SHAPE", -3: "SPECV_E_DTYPE", -4: "SPECV_E_TEMP",
-          -5: "SPECV_E_WORKSPACE", -6: "SPECV_E_ALIGN", -7: "SPECV_E_HIP", -8: "SPECV_E_ARG"}
+          -5: "SPECV_E_WORKSPACE", -6: "SPECV_E_ALIGN", -7: "SPECV_E_HIP"}
 
 # every symbol include/specverify.h declares
 EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_ex", "spec_verify_strerror",
@@ -53,7 +52,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     common = [vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, i32, vp, sz, vp]
     lib.spec_verify.argtypes = common
     lib.spec_verify.restype = i32
-    lib.spec_verify_ex.argtypes = common + [vp, vp, i32, vp, vp]
+    lib.spec_verify_ex.argtypes = common + [vp, vp, vp, vp]
     lib.spec_verify_ex.restype = i32
     lib.spec_verify_strerror.argtypes = [i32]
     lib.spec_verify_strerror.restype = ctypes.c_char_p
@@ -91,8 +90,7 @@ def _ptr(t) -> Optional[int]:
 
 def spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float,
                 out_tokens=None, out_n_accepted=None, workspace=None, *,
-                out_logz=None, out_flags=None, draw_policy: int = DRAW_CERTIFIED,
-                events=None, stream=None, extended: bool = False) -> int:
+                out_logz=None, out_flags=None, events=None, stream=None, extended: bool = False) -> int:
     """Raw call with caller-provided device tensors; returns the library's status code."""
     lib = load()
     B, K1, V = logits_p.shape
@@ -103,15 +101,14 @@ def spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float
     args = [_ptr(logits_p), _ptr(logits_q), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resample),
             float(T), B, K, V, _ptr(out_tokens), _ptr(out_n_accepted), dt,
             _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(), st]
-    if not extended and out_logz is None and out_flags is None and draw_policy == DRAW_CERTIFIED and events is None:
+    if not extended and out_logz is None and out_flags is None and events is None:
         return int(lib.spec_verify(*args))
     e0, e1 = events if events is not None else (None, None)
-    return int(lib.spec_verify_ex(*args, _ptr(out_logz), _ptr(out_flags), draw_policy, e0, e1))
+    return int(lib.spec_verify_ex(*args, _ptr(out_logz), _ptr(out_flags), e0, e1))
 
 
 def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
-           return_logz: bool = False, return_flags: bool = False, draw_policy: int = DRAW_CERTIFIED,
-           workspace=None, events=None):
+           return_logz: bool = False, return_flags: bool = False, workspace=None, events=None):
     """One verify step on torch device tensors.
 
     logits_p [B,K+1,V] and logits_q [B,K,V] (bf16 or fp32, contiguous, same
@@ -155,7 +152,7 @@ def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
     logz = torch.empty((B, 2 * K + 1), dtype=torch.float32, device=dev) if return_logz else None
     flags = torch.empty((B,), dtype=torch.int32, device=dev) if return_flags else None
     rc = spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T, tokens, n_acc, workspace,
-                     out_logz=logz, out_flags=flags, draw_policy=draw_policy, events=events)
+                     out_logz=logz, out_flags=flags, events=events)
     if rc != 0:
         raise SpecVerifyError(rc, strerror(rc))
     out = (tokens, n_acc)

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["api.cpp", "k_sweep.hip", "k_scan.hip", "k_draw.hip", "k_refine.hip"]
+SOURCES = ["api.cpp", "k_sweep.hip", "k_scan.hip", "k_draw.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,6 +1,7 @@
 // Host side of libspecverify: argument checks, workspace layout and the
 // launch sequence of one verify step.  Nothing here allocates, synchronises
 // or keeps state between calls.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -16,20 +17,6 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int elt_bytes(int dtype) { return dtype == SPECV_BF16 ? 2 : 4; }
-
-// Error model of the fp32 draw, in units of u = 2^-24.  The sweep forms
-// t = fma(x, c, -R) with R = rint(row-share max * c), so t <= 1/2 and its one
-// rounding is at most u|t|; v_exp_f32 is taken as <= 2 ulp; lane sums add a
-// tree of 8 and six adds; merges are exact power-of-two rescales in fp64.
-// The draw forms log2 p = fma(x, c, -whole) - fraction (two roundings of
-// size u |log2 p| + u/2) and a v_exp_f32.  c = log2(e)/T is itself rounded,
-// which acts as a relative temperature change of at most u.  Weighted by p,
-// |log2 p| averages at most log2 V, so each normalised row's prefix masses
-// carry a relative error of at most u (7 ln V + 12) + 2 exp errors.
-double row_error(int V) {
-  const double u = std::ldexp(1.0, -24);
-  return u * (7.0 * std::log(static_cast<double>(V)) + 12.0 + 8.0);
-}
 
 }  // namespace
 
@@ -53,24 +40,22 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
     L.total = off;
     return L;
   }
-  // draw / refine chunks: multiples of 2048 elements, at most kMaxDrawChunks per row
+  // draw chunks: multiples of 2048 elements, at most kMaxDrawChunks per row
   long ch = 4096;
   const long need = (static_cast<long>(V) + kMaxDrawChunks - 1) / kMaxDrawChunks;
   if (need > ch) ch = (need + 2047) / 2048 * 2048;
-  L.ch3 = L.ch4 = static_cast<int>(ch);
-  L.R3 = L.R4 = static_cast<int>((V + ch - 1) / ch);
+  L.ch3 = static_cast<int>(ch);
+  L.R3 = static_cast<int>((V + ch - 1) / ch);
   L.rec = off;
   off = align_up(off + static_cast<size_t>(B) * sizeof(SeqRec));
-  L.cnt = off;
-  off = align_up(off + sizeof(uint32_t));
   L.csum = off;
-  off = align_up(off + static_cast<size_t>(B) * L.R3 * sizeof(double));
-  L.list = off;
+  off = align_up(off + static_cast<size_t>(B) * L.R3 * 5 * sizeof(double));
+  L.xsum = off;
+  off = align_up(off + static_cast<size_t>(B) * L.R3 * 5 * sizeof(double));
+  L.queue = off;
   off = align_up(off + static_cast<size_t>(B) * sizeof(int32_t));
-  L.rpart = off;
-  off = align_up(off + static_cast<size_t>(B) * 2 * L.R4 * sizeof(double2));
-  L.rsum = off;
-  off = align_up(off + static_cast<size_t>(B) * L.R4 * sizeof(double2));
+  L.qcount = off;
+  off = align_up(off + sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -113,8 +98,7 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
                    const float* u_accept, const float* u_resample, float T, int B, int K, int V,
                    int32_t* out_tokens, int32_t* out_n_accepted, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream,
-                   float* out_logz, int32_t* out_flags, int draw_policy,
-                   void* ev_sweep_begin, void* ev_sweep_end) {
+                   float* out_logz, int32_t* out_flags, void* ev_sweep_begin, void* ev_sweep_end) {
   using namespace sv;
   if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_E_DTYPE;
   if (!valid_temperature(T)) return SPECV_E_TEMP;
@@ -122,7 +106,6 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   if (!logits_p || !draft_tokens || !out_tokens || !out_n_accepted) return SPECV_E_NULL;
   if (!greedy && (!logits_q || !u_accept || !u_resample)) return SPECV_E_NULL;
   if (!valid_shape(B, K, V, greedy)) return SPECV_E_SHAPE;
-  if (draw_policy < SPECV_DRAW_CERTIFIED || draw_policy > SPECV_DRAW_FP32) return SPECV_E_ARG;
   const uintptr_t eb = static_cast<uintptr_t>(elt_bytes(dtype));
   const uintptr_t ap = reinterpret_cast<uintptr_t>(logits_p);
   const uintptr_t aq = greedy ? 0 : reinterpret_cast<uintptr_t>(logits_q);
@@ -147,8 +130,9 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   P.out_n = out_n_accepted;
   P.out_logz = out_logz;
   P.out_flags = out_flags;
-  P.policy = draw_policy;
   P.part = reinterpret_cast<float2*>(ws + L.part);
+  P.seq0 = 0;
+  P.nseq = B;
   P.nch1 = L.nch1;
   P.ch1 = L.ch1;
   P.cq = L.cq;
@@ -158,40 +142,27 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   const bool timed = e0 && e1;
 
   if (greedy) {
-    if (timed && hipEventRecord(e0, st) != hipSuccess) return SPECV_E_HIP;
-    if (launch_sweep_argmax(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
-    if (timed && hipEventRecord(e1, st) != hipSuccess) return SPECV_E_HIP;
+    if (launch_sweep_argmax(P, dtype, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
+      return SPECV_E_HIP;
     if (launch_greedy_scan(P, st) != hipSuccess) return SPECV_E_HIP;
     return SPECV_OK;
   }
 
   const double T64 = static_cast<double>(T);
-  P.c = static_cast<float>(M_LOG2E / T64);
+  const double c64 = M_LOG2E / T64;
+  P.c = static_cast<float>(c64);
   P.inv_t = 1.0 / T64;
-  const double u = std::ldexp(1.0, -24);
-  const double lnV = std::log(static_cast<double>(V));
-  // residual draw: |C' - C| and |t' - t| each within 2 (row error + 17u), twice for safety
-  P.e_abs_res = 2.0 * 4.0 * (row_error(V) + 17.0 * u);
-  // bonus draw: only per-element rounding and the chunk sums remain (normaliser cancels)
-  P.e_rel_bonus = 2.0 * 2.0 * u * (3.0 * lnV + 21.0);
   P.rec = reinterpret_cast<SeqRec*>(ws + L.rec);
-  P.list_count = reinterpret_cast<uint32_t*>(ws + L.cnt);
   P.csum = reinterpret_cast<double*>(ws + L.csum);
-  P.list = reinterpret_cast<int32_t*>(ws + L.list);
-  P.rpart = reinterpret_cast<double2*>(ws + L.rpart);
-  P.rsum = reinterpret_cast<double2*>(ws + L.rsum);
+  P.xsum = reinterpret_cast<double*>(ws + L.xsum);
+  P.queue = reinterpret_cast<int32_t*>(ws + L.queue);
+  P.qcount = reinterpret_cast<uint32_t*>(ws + L.qcount);
   P.R3 = L.R3;
   P.ch3 = L.ch3;
-  P.R4 = L.R4;
-  P.ch4 = L.ch4;
-  P.refine_grid = (B < 64 ? B : 64) * L.R4;
 
-  if (timed && hipEventRecord(e0, st) != hipSuccess) return SPECV_E_HIP;
-  if (launch_sweep_lse(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
-  if (timed && hipEventRecord(e1, st) != hipSuccess) return SPECV_E_HIP;
+  if (launch_sweep_lse(P, dtype, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess) return SPECV_E_HIP;
   if (launch_accept_scan(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   if (launch_draw(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
-  if (launch_refine(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   return SPECV_OK;
 }
 
@@ -200,8 +171,8 @@ int spec_verify(const void* logits_p, const void* logits_q, const int32_t* draft
                 int32_t* out_tokens, int32_t* out_n_accepted, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream) {
   return spec_verify_ex(logits_p, logits_q, draft_tokens, u_accept, u_resample, T, B, K, V, out_tokens,
-                        out_n_accepted, dtype, workspace, workspace_bytes, stream, nullptr, nullptr,
-                        SPECV_DRAW_CERTIFIED, nullptr, nullptr);
+                        out_n_accepted, dtype, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr,
+                        nullptr);
 }
 
 const char* spec_verify_strerror(int code) {
@@ -214,7 +185,6 @@ const char* spec_verify_strerror(int code) {
     case SPECV_E_WORKSPACE: return "workspace NULL, not 256-byte aligned, or too small";
     case SPECV_E_ALIGN: return "logits pointer not aligned to its element size";
     case SPECV_E_HIP: return "a HIP launch failed";
-    case SPECV_E_ARG: return "argument out of range";
     default: return "unknown error";
   }
 }

@@ -17,17 +17,13 @@
 // before it computes.  A row is split into chunks of equal size, one
 // workgroup each, so no workgroup gets a short tail; each wave writes its own
 // partial, so no workgroup barrier holds finished waves back.
+#include <hip/hip_ext.h>
+
 #include "sv_device.h"
 
 namespace sv {
 
 namespace {
-
-// Reset the refine queue.  The first kernel of a call does it, so stream
-// order makes the zero visible to the draw that appends to the queue.
-__device__ inline void reset_queue(const Params& p) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) p.list_count[0] = 0u;
-}
 
 // Row `row` of the sampling sweep: K+1 target rows then K draft rows per
 // sequence.  32-bit division: row counts are checked on the host.
@@ -73,11 +69,11 @@ __device__ inline void load_chunk(const Params& p, const void* r, uint32_t chunk
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
-  reset_queue(p);
   constexpr int N = kSweepElems<DT, VEC>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  const uint32_t row = blockIdx.x / static_cast<uint32_t>(p.nch1);
-  const uint32_t chunk = blockIdx.x - row * static_cast<uint32_t>(p.nch1);
+  const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);
+  const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
+  const uint32_t row = static_cast<uint32_t>(p.seq0) * (2u * p.K + 1u) + local;
   const float c = p.c;
   float e[N];
   long lo, hi;
@@ -115,8 +111,9 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
   constexpr int N = kSweepElems<DT, VEC>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  const uint32_t row = blockIdx.x / static_cast<uint32_t>(p.nch1);  // target rows only: s * (K+1) + k
-  const uint32_t chunk = blockIdx.x - row * static_cast<uint32_t>(p.nch1);
+  const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);  // target rows only: s * (K+1) + k
+  const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
+  const uint32_t row = static_cast<uint32_t>(p.seq0) * (p.K + 1u) + local;
   float e[N];
   long lo, hi;
   load_chunk<DT, VEC>(p, row_ptr<DT>(p.lp, row, p.V), chunk, e, lo, hi);
@@ -139,30 +136,31 @@ __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
 
 }  // namespace
 
-hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t st) {
-  const long rows = static_cast<long>(p.B) * (2 * p.K + 1);
-  const dim3 grid(static_cast<unsigned>(rows * p.nch1)), block(kBlock);
-  if (dtype == 1) {
-    if (p.vec) hipLaunchKernelGGL((k_sweep_lse<1, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((k_sweep_lse<1, false>), grid, block, 0, st, p);
-  } else {
-    if (p.vec) hipLaunchKernelGGL((k_sweep_lse<0, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((k_sweep_lse<0, false>), grid, block, 0, st, p);
-  }
+// Events, when given, are recorded as part of the dispatch itself (no
+// separate marker packet, so no bubble between kernels).
+template <typename Kern>
+hipError_t launch_evented(Kern k, const dim3& grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1, const Params& p) {
+  if (e0 || e1) hipExtLaunchKernelGGL(k, grid, dim3(kBlock), 0, st, e0, e1, 0, p);
+  else hipLaunchKernelGGL(k, grid, dim3(kBlock), 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t st) {
-  const long rows = static_cast<long>(p.B) * (p.K + 1);
-  const dim3 grid(static_cast<unsigned>(rows * p.nch1)), block(kBlock);
-  if (dtype == 1) {
-    if (p.vec) hipLaunchKernelGGL((k_sweep_argmax<1, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((k_sweep_argmax<1, false>), grid, block, 0, st, p);
-  } else {
-    if (p.vec) hipLaunchKernelGGL((k_sweep_argmax<0, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((k_sweep_argmax<0, false>), grid, block, 0, st, p);
-  }
-  return hipGetLastError();
+hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const long rows = static_cast<long>(p.nseq) * (2 * p.K + 1);
+  const dim3 grid(static_cast<unsigned>(rows * p.nch1));
+  if (dtype == 1) return p.vec ? launch_evented(k_sweep_lse<1, true>, grid, st, e0, e1, p)
+                               : launch_evented(k_sweep_lse<1, false>, grid, st, e0, e1, p);
+  return p.vec ? launch_evented(k_sweep_lse<0, true>, grid, st, e0, e1, p)
+               : launch_evented(k_sweep_lse<0, false>, grid, st, e0, e1, p);
+}
+
+hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const long rows = static_cast<long>(p.nseq) * (p.K + 1);
+  const dim3 grid(static_cast<unsigned>(rows * p.nch1));
+  if (dtype == 1) return p.vec ? launch_evented(k_sweep_argmax<1, true>, grid, st, e0, e1, p)
+                               : launch_evented(k_sweep_argmax<1, false>, grid, st, e0, e1, p);
+  return p.vec ? launch_evented(k_sweep_argmax<0, true>, grid, st, e0, e1, p)
+               : launch_evented(k_sweep_argmax<0, false>, grid, st, e0, e1, p);
 }
 
 }  // namespace sv

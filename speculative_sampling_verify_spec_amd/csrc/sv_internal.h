@@ -20,16 +20,12 @@ constexpr int kSweepElems() {
 }
 
 // Per-sequence record written by the acceptance scan and read by the draw.
-// A row's log2 normaliser log2 sum_v 2^(x_v * c) (c = log2(e)/T in fp32) is
-// stored as a whole number plus a fraction in [-1/2, 1/2], so the draw forms
-// log2 p(v) = fma(x_v, c, -whole) - fraction with a single large rounding.
 struct SeqRec {
   int32_t n;       // accepted draft tokens
   int32_t flags;   // SPECV_FLAG_* set so far
-  float mp, mq;    // whole parts of the decisive target / draft row's log2 normaliser
-  double lp2, lq2; // their fractional parts
+  double lzp, lzq; // log2 sum_v 2^(x_v c) of the decisive target / draft row (fp32-accurate)
 };
-static_assert(sizeof(SeqRec) == 32, "SeqRec layout");
+static_assert(sizeof(SeqRec) == 24, "SeqRec layout");
 
 // Everything a kernel needs, passed by value.
 struct Params {
@@ -40,44 +36,38 @@ struct Params {
   const float* ur;           // [B]
   int B, K, V;
   int vec;                   // 1: 16-byte vector loads are legal for every row
-  float c;                   // log2(e) / T rounded to fp32 (fast path)
-  double inv_t;              // 1 / T in fp64 (refine path)
+  float c;                   // log2(e) / T rounded to fp32
+  double inv_t;              // 1 / T in fp64 (exact draw)
   int32_t* out_tokens;       // [B][K+1]
   int32_t* out_n;            // [B]
   float* out_logz;           // [B][2K+1] or null
   int32_t* out_flags;        // [B] or null
-  int policy;                // SPECV_DRAW_*
-  double e_abs_res;          // certified bound, residual draws (probability-mass units)
-  double e_rel_bonus;        // certified bound, bonus draws (relative to the row's own sum)
   // workspace
   float2* part;              // [rows][nch1][kWaves] (R, s) sweep partials, or (max, index bits) in greedy mode
   SeqRec* rec;               // [B]
-  uint32_t* list_count;      // [1] number of sequences queued for the fp64 refine
-  int32_t* list;             // [B] their ids
-  double* csum;              // [B][R3] draw chunk sums
-  double2* rpart;            // [B][2][R4] refine (max, sum) partials
-  double2* rsum;             // [B][R4] refine chunk sums (residual, target)
+  double* csum;              // [B][R3][5] fast draw chunk sums
+  double* xsum;              // [B][R3][5] exact draw chunk sums (queued sequences)
+  uint32_t* qcount;          // [1] sequences queued for the exact draw
+  int32_t* queue;            // [B] their ids (from the first sequence of the launch on)
   int nch1, ch1;             // sweep chunks per row, elements per sweep chunk (at most)
   int cq, cr;                // sweep chunk c spans c*cq + min(c, cr) .. + cq + (c < cr) units
   int R3, ch3;               // draw chunks per row, elements per draw chunk
-  int R4, ch4;               // refine chunks per row, elements per refine chunk
-  int refine_grid;           // workgroups of each refine launch
+  int seq0, nseq;            // the sequences a launch covers
 };
 
 // Workspace layout (byte offsets), shared by spec_verify_workspace_size and the launcher.
 struct Layout {
-  size_t part, rec, cnt, csum, list, rpart, rsum, total;
-  int nch1, ch1, cq, cr, R3, ch3, R4, ch4;
+  size_t part, rec, csum, xsum, queue, qcount, total;
+  int nch1, ch1, cq, cr, R3, ch3;
 };
 
 Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy);
 
 // Launchers (one per kernel), defined next to their kernels.
-hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t s);
-hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_accept_scan(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_greedy_scan(const Params& p, hipStream_t s);
 hipError_t launch_draw(const Params& p, int dtype, hipStream_t s);
-hipError_t launch_refine(const Params& p, int dtype, hipStream_t s);
 
 }  // namespace sv

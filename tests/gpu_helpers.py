@@ -5,11 +5,11 @@ import workloads
 from oracle.parity import GpuOut
 
 
-def run_gpu(sv, batch, policy=0, dev_inputs=None) -> GpuOut:
+def run_gpu(sv, batch, dev_inputs=None) -> GpuOut:
     import torch
     lp, lq, x, ua, ur = dev_inputs if dev_inputs is not None else workloads.to_device(batch)
     greedy = batch.T == 0.0
-    out = sv.verify(lp, lq, x, ua, ur, batch.T, return_logz=not greedy, return_flags=True, draw_policy=policy)
+    out = sv.verify(lp, lq, x, ua, ur, batch.T, return_logz=not greedy, return_flags=True)
     torch.cuda.synchronize()
     if greedy:
         tok, n, flags = out

@@ -31,9 +31,6 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     consts = dict((k, int(v)) for k, v in re.findall(r"#define\s+(SPECV_\w+)\s+(-?\d+)", text))
     assert consts["SPECV_MAX_K"] == sv.SPECV_MAX_K
-    assert consts["SPECV_DRAW_CERTIFIED"] == sv.DRAW_CERTIFIED
-    assert consts["SPECV_DRAW_FP64"] == sv.DRAW_FP64 and consts["SPECV_DRAW_FP32"] == sv.DRAW_FP32
-    assert consts["SPECV_FLAG_REFINED"] == sv.FLAG_REFINED
     assert consts["SPECV_FLAG_ZW_ZERO"] == sv.FLAG_ZW_ZERO and consts["SPECV_FLAG_BAD_DRAFT"] == sv.FLAG_BAD_DRAFT
     for code, name in sv.ERRORS.items():
         assert consts.get(name, 0) == code, name
@@ -65,11 +62,11 @@ WS = 0x7000000
 
 def _call(lib, **kw):
     a = dict(lp=P, lq=Q, x=X, ua=UA, ur=UR, T=1.0, B=4, K=3, V=128, ot=OT, on=ON, dtype=F32,
-             ws=WS, wsb=1 << 30, stream=None, logz=None, flags=None, policy=0)
+             ws=WS, wsb=1 << 30, stream=None, logz=None, flags=None)
     a.update(kw)
     return lib.spec_verify_ex(a["lp"], a["lq"], a["x"], a["ua"], a["ur"], a["T"], a["B"], a["K"], a["V"],
                               a["ot"], a["on"], a["dtype"], a["ws"], a["wsb"], a["stream"], a["logz"],
-                              a["flags"], a["policy"], None, None)
+                              a["flags"], None, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -79,7 +76,6 @@ def _call(lib, **kw):
     (dict(lq=None), -1), (dict(ua=None), -1), (dict(ur=None), -1),
     (dict(B=0), -2), (dict(K=0), -2), (dict(K=33), -2), (dict(V=0), -2), (dict(B=-3), -2),
     (dict(B=1 << 30, V=1 << 30), -2),
-    (dict(policy=3), -8), (dict(policy=-1), -8),
     (dict(lp=P + 2), -6), (dict(lq=Q + 1, dtype=BF16), -6),
     (dict(ws=None), -5), (dict(ws=WS + 8), -5), (dict(wsb=1024), -5),
 ])

@@ -39,7 +39,7 @@ def test_workload_full_size(gpu_lib, cfg):
     g = run_gpu(gpu_lib, b)
     ref = oracle.verify_batch(b)
     rep = compare(b, g, ref)
-    say(f"[parity] workload {cfg}: decisions={rep.decisions} excused={rep.excused} refined={rep.refined} "
+    say(f"[parity] workload {cfg}: decisions={rep.decisions} excused={rep.excused} "
         f"max_logz_err={rep.max_logz_err:.2e}")
     rep.check()
 
@@ -93,24 +93,18 @@ def test_sharp_fp32_workload_full_size_sampled(gpu_lib):
     assert np.all((emitted >= 0) & (emitted < V))
 
 
-@pytest.mark.parametrize("policy", [1, 2])
 @pytest.mark.parametrize("cfg", [1, 2])
-def test_draw_policies(gpu_lib, cfg, policy):
-    """fp64 draw everywhere must match the oracle; the fp32-only draw may differ
-    only where the oracle's margin is inside the fast path's error bound."""
+def test_draw_matches_oracle_exactly(gpu_lib, cfg):
+    """The draw is computed in fp64: every drawn token must equal the oracle's
+    whenever the acceptance decisions agree, with no excuse needed (the oracle
+    margin of every draw on these batches is far above the fp64 error)."""
     b = full_batch(cfg)
-    g = run_gpu(gpu_lib, b, policy=policy)
+    g = run_gpu(gpu_lib, b)
     ref = oracle.verify_batch(b)
-    rep = compare(b, g, ref)
-    say(f"[parity] workload {cfg} policy {policy}: excused={rep.excused} refined={rep.refined}")
-    if policy == 1:
-        assert rep.refined == b.B
-        rep.check()
-    else:
-        assert rep.refined == 0
-        assert not [f for f in rep.failures if f[1] != "draw"], rep.failures[:3]
-        bound = 4e-4  # normalised; the certified bound divided by the residual mass is below this here
-        assert all(f[4] < bound for f in rep.failures), rep.failures[:5]
+    same_n = g.n == ref.n_accepted
+    rows = np.flatnonzero(same_n)
+    assert len(rows) >= b.B - 1
+    np.testing.assert_array_equal(g.tokens[rows], ref.tokens[rows])
 
 
 SMALL = [
@@ -128,9 +122,8 @@ def test_small_and_ragged_shapes(gpu_lib, shape):
     wl = workloads.Workload("small", B, K, V, dt, float(np.float32(T)), 2.0, 1.1, "noise", 0.8)
     b = workloads.make_batch(1, wl=wl, seed=100 + V + K)
     say(f"[parity] small {wl.describe()}")
-    for policy in (0, 1):
-        rep = compare(b, run_gpu(gpu_lib, b, policy=policy), oracle.verify_batch(b))
-        rep.check()
+    rep = compare(b, run_gpu(gpu_lib, b), oracle.verify_batch(b))
+    rep.check()
 
 
 @pytest.mark.parametrize("shape", [(3, 2, 1001), (4, 8, 4096), (2, 32, 777), (6, 4, 50000)])
