@@ -2,7 +2,8 @@
 """Throughput of the speculative-sampling verify step on one MI355X.
 
 One step = one call of the whole verify path (row sweep, acceptance scan,
-draw, conditional fp64 refine) over one batch of the headline workload:
+replacement/bonus draw with its fp64 fallback for uncertified draws) over
+one batch of the headline workload:
 B=256 sequences, K=8 drafts, V=128256, bf16 logits, T=0.7.  Inputs are
 generated on the host, copied to HBM once, and stay resident; the timed
 region is K back-to-back steps between two synchronisations.  The whole
@@ -12,6 +13,12 @@ a previous step's cache.
 Prints one JSON line.  `roofline` describes the dominant kernel (the row
 sweep), timed with HIP events recorded around it inside every timed step;
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same batch.
+
+--copy-calibration BYTES first runs three plain device-to-device copies of
+that many bytes, so that a rocprofv3 counter pass over the same process
+(FETCH_SIZE, WRITE_SIZE) also measures a kernel of known traffic: the ratio
+of its known bytes to its counter reading scales the sweep's counters to
+bytes.
 """
 from __future__ import annotations
 
@@ -106,6 +113,7 @@ def main():
     ap.add_argument("--workload", type=int, default=HEADLINE, choices=range(5))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verify step is data-parallel "
@@ -119,6 +127,14 @@ def main():
     import workloads
 
     sv.load()
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 device copies of {args.copy_calibration} bytes")
+        del src, dst
     wl = workloads.WORKLOADS[args.workload]
     log(f"generating {wl.name}: {wl.describe()}")
     t0 = time.perf_counter()
