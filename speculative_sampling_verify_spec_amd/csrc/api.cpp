@@ -40,7 +40,7 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
     L.total = off;
     return L;
   }
-  // draw chunks: multiples of 2048 elements, at most kMaxDrawChunks per row
+  // fp64 draw chunks: multiples of 2048 elements, at most kMaxDrawChunks per row
   long ch = 4096;
   const long need = (static_cast<long>(V) + kMaxDrawChunks - 1) / kMaxDrawChunks;
   if (need > ch) ch = (need + 2047) / 2048 * 2048;
@@ -48,8 +48,6 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
   L.R3 = static_cast<int>((V + ch - 1) / ch);
   L.rec = off;
   off = align_up(off + static_cast<size_t>(B) * sizeof(SeqRec));
-  L.csum = off;
-  off = align_up(off + static_cast<size_t>(B) * L.R3 * 5 * sizeof(double));
   L.xsum = off;
   off = align_up(off + static_cast<size_t>(B) * L.R3 * 5 * sizeof(double));
   L.queue = off;
@@ -153,7 +151,6 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   P.c = static_cast<float>(c64);
   P.inv_t = 1.0 / T64;
   P.rec = reinterpret_cast<SeqRec*>(ws + L.rec);
-  P.csum = reinterpret_cast<double*>(ws + L.csum);
   P.xsum = reinterpret_cast<double*>(ws + L.xsum);
   P.queue = reinterpret_cast<int32_t*>(ws + L.queue);
   P.qcount = reinterpret_cast<uint32_t*>(ws + L.qcount);
@@ -161,8 +158,8 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   P.ch3 = L.ch3;
 
   if (launch_sweep_lse(P, dtype, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess) return SPECV_E_HIP;
-  if (launch_accept_scan(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
-  if (launch_draw(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
+  if (launch_verify(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
+  if (launch_exact(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   return SPECV_OK;
 }
 

@@ -1,0 +1,370 @@
+// The fp64 draw, for the sequences whose fast draw could not be certified.
+//
+// The draw is the same inverse CDF as the fast one (the smallest token v
+// whose running sum C(v) of w exceeds t = u Z; w = max(0, p_n - q_n) after a
+// rejection at n < K, w = p_K after K acceptances), with fp64 weights
+// P(v) = exp(x/T - L'p), Q(v) = exp(y/T - L'q) normalised by their own sums:
+// w = max(0, P - rho Q) / sum P with rho = sum P / sum Q.
+//
+// Two kernels walk the queue the fast draw filled:
+//   exact_chunks (queued sequences x chunks of ch3 tokens): per chunk
+//        sum P, sum Q, A = sum max(0, P - Q), G = sum_{P > Q} Q and
+//        H = sum_{near flip} Q, the Q-mass within a relative kKappa of P = Q.
+//        The chunk's residual mass at the exact rho is A - (rho - 1) G up to
+//        the mass of tokens whose sign flips, which is at most |rho - 1| H.
+//   exact_select (one workgroup per queued sequence): rho and the corrected
+//        chunk sums give Z and the chunk holding t; that chunk is rescanned
+//        (lane-contiguous runs, fp64 scan over 512 threads) with the exact
+//        rho.  When t may lie before the located chunk (within the
+//        corrections' error) the rescan starts from the first chunk; when rho
+//        leaves the linearisation window the total is recomputed exactly
+//        first.
+// Per weight the error is ~1e-16 relative (exp_f64), so the token matches the
+// exact inverse CDF unless t lies within ~1e-12 of an edge.  Past the end the
+// draw takes the last token with positive weight; a residual of zero mass
+// (p == q to rounding) falls back to p_n and sets a flag.
+#include "sv_device.h"
+#include "specverify.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int kSelBlock = 512;                   // threads of the select workgroup
+constexpr int kSelWaves = kSelBlock / kWave;
+constexpr int kRun = 8;                          // elements per lane per rescan round (a whole bf16 vector)
+constexpr int kRound = kSelBlock * kRun;         // 4096 elements per round (one chunk)
+constexpr double kKappa = 1e-4;                  // near-flip window, relative to Q
+constexpr unsigned kExactSeqs = 32;              // queued sequences the kernels cover per pass
+
+// fp64 weight exp(x / T - L'), L' the natural-log reference.
+struct ExactWeight {
+  double inv_t, ap, aq;
+  __device__ double P(float x) const { return exp_f64(static_cast<double>(x) * inv_t - ap); }
+  __device__ double Q(float x) const { return exp_f64(static_cast<double>(x) * inv_t - aq); }
+};
+
+__device__ inline ExactWeight exact_weight(const Params& p, const SeqRec& rec) {
+  ExactWeight e;
+  e.inv_t = p.inv_t;
+  e.ap = rec.lzp * M_LN2;
+  e.aq = rec.lzq * M_LN2;
+  return e;
+}
+
+template <int DT>
+struct Rows {
+  const void* rp;
+  const void* rq;  // null for a bonus draw
+};
+
+template <int DT>
+__device__ inline Rows<DT> decisive_rows(const Params& p, long s, int n) {
+  Rows<DT> r;
+  r.rp = row_ptr<DT>(p.lp, s * (p.K + 1) + n, p.V);
+  r.rq = n == p.K ? nullptr : row_ptr<DT>(p.lq, s * p.K + n, p.V);
+  return r;
+}
+
+// ------------------------------------------------------------ chunk sums --
+// Chunk r of the decisive row(s) -> out[0..4] = sum P, sum Q, A, G, H (only
+// out[0] for a bonus draw).  Loads go out branch-free, U units per lane, and
+// are widened one unit at a time; the five sums are reduced over the
+// workgroup together.
+template <int DT, bool VEC>
+__device__ inline void exact_chunk_sums(const Params& p, const Rows<DT>& rows, const ExactWeight& wt, bool bonus,
+                                        int r, double* out) {
+  const long lo = static_cast<long>(r) * p.ch3;
+  const long hi = min(static_cast<long>(p.V), lo + p.ch3);
+  constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
+  constexpr int U = VEC ? 2 : 8;
+  const long ulo = lo / PV, uhi = hi / PV;  // VEC: lo and hi are multiples of PV
+  double acc[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+  for (long r0 = ulo; r0 < uhi; r0 += static_cast<long>(kBlock) * U) {
+    uint4 rp[VEC ? U : 1], rq[VEC ? U : 1];
+    float sp_[VEC ? 1 : U], sq_[VEC ? 1 : U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const long u = r0 + threadIdx.x + static_cast<long>(i) * kBlock;
+      if constexpr (VEC) {
+        const long uu = u < uhi ? u : uhi - 1;
+        rp[i] = load16(rows.rp, uu);
+        if (!bonus) rq[i] = load16(rows.rq, uu);
+      } else {
+        sp_[i] = load_masked<DT>(rows.rp, u, uhi);
+        sq_[i] = bonus ? -INFINITY : load_masked<DT>(rows.rq, u, uhi);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      float ep[PV], eq[PV];
+      if constexpr (VEC) {
+        Elt<DT>::unpack(rp[i], ep);
+        if (!bonus) Elt<DT>::unpack(rq[i], eq);
+        if (bonus || r0 + threadIdx.x + static_cast<long>(i) * kBlock >= uhi) {
+#pragma unroll
+          for (int k = 0; k < PV; ++k) eq[k] = -INFINITY;
+        }
+        if (r0 + threadIdx.x + static_cast<long>(i) * kBlock >= uhi) {
+#pragma unroll
+          for (int k = 0; k < PV; ++k) ep[k] = -INFINITY;
+        }
+      } else {
+        ep[0] = sp_[i];
+        eq[0] = sq_[i];
+      }
+      double sp = 0.0, sq = 0.0, a = 0.0, g = 0.0, h = 0.0;
+#pragma unroll
+      for (int k = 0; k < PV; ++k) {
+        const double P = wt.P(ep[k]);
+        const double Q = wt.Q(eq[k]);  // 0 for -inf
+        const double d = P - Q;
+        sp += P;
+        sq += Q;
+        a += d > 0.0 ? d : 0.0;
+        g += d > 0.0 ? Q : 0.0;
+        h += (d <= kKappa * Q && -d <= kKappa * Q) ? Q : 0.0;
+      }
+      acc[0] += sp;
+      acc[1] += sq;
+      acc[2] += a;
+      acc[3] += g;
+      acc[4] += h;
+    }
+  }
+  __shared__ double lds[kWaves][5];
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+#pragma unroll
+  for (int k = 0; k < 5; ++k) acc[k] = wave_sum(acc[k]);
+  __syncthreads();  // the previous item's reads of lds are done
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < 5; ++k) lds[w][k] = acc[k];
+  }
+  __syncthreads();
+  if (threadIdx.x < 5) {
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) t += lds[i][threadIdx.x];
+    if (!bonus || threadIdx.x == 0) out[threadIdx.x] = t;
+  }
+}
+
+// A lane's run of kRun consecutive logits from v0, -inf at and past chi.
+// VEC: v0 and chi are multiples of the vector width, so whole 16-byte units
+// are loaded (index clamped below chi) and masked.
+template <int DT, bool VEC>
+__device__ inline void load_run(const void* row, long v0, long chi, float (&e)[kRun]) {
+  if constexpr (VEC) {
+    constexpr int PV = Elt<DT>::kPerVec;
+    constexpr int NU = kRun / PV;
+    static_assert(kRun % PV == 0, "whole units per run");
+    const long u0 = v0 / PV, uend = chi / PV;
+    uint4 raw[NU];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) raw[i] = load16(row, u0 + i < uend ? u0 + i : uend - 1);
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      Elt<DT>::unpack(raw[i], &e[i * PV]);
+      if (u0 + i >= uend) {
+#pragma unroll
+        for (int k = 0; k < PV; ++k) e[i * PV + k] = -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) e[k] = load_masked<DT>(row, v0 + k, chi);
+  }
+}
+
+// ---------------------------------------------------------------- select --
+// The draw for one queued sequence from its chunk sums (whole workgroup).
+// Thread 0 gets the token and whether the zero-mass fallback was used.
+template <int DT, bool VEC>
+__device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const ExactWeight& wt, bool bonus,
+                                    const double* cs_base, double ur, int* token, bool* zw_zero) {
+  const int lane = threadIdx.x % kWave;
+  __shared__ double s_rho, s_t;
+  __shared__ double s_base;
+  __shared__ int s_chunk, s_usep, s_exact_total;
+  if (threadIdx.x < kWave) {
+    const bool have = lane < p.R3;
+    const double* cs = cs_base + (have ? lane : 0) * 5;
+    const double sp = have ? cs[0] : 0.0;
+    const double SP = wave_sum(sp);
+    double v = sp, rho = 1.0, err = 0.0;
+    int usep = 1;
+    if (!bonus) {
+      const double sq = have ? cs[1] : 0.0, a = have ? cs[2] : 0.0;
+      const double g = have ? cs[3] : 0.0, h = have ? cs[4] : 0.0;
+      const double SQ = wave_sum(sq);
+      rho = SP / SQ;
+      // first-order correction to the exact rho, with its error bound
+      const double corrected = fmax(a - (rho - 1.0) * g, 0.0);
+      const double Z = wave_sum(corrected);
+      usep = !(Z > 0.0);  // p == q to rounding: draw from p_n instead
+      v = usep ? sp : corrected;
+      err = usep ? 0.0 : fabs(rho - 1.0) * h;
+    }
+    const double inc = wave_inclusive_scan(v);
+    const double err_inc = wave_inclusive_scan(err);
+    double excl = __shfl_up(inc, 1, kWave), err_excl = __shfl_up(err_inc, 1, kWave);
+    if (lane == 0) excl = err_excl = 0.0;
+    const double z = __shfl(inc, kWave - 1, kWave);
+    const double t = ur * z;
+    const uint64_t hit = __ballot(have && inc > t);
+    const uint64_t pos = __ballot(have && v > 0.0);
+    int rc;
+    if (hit) rc = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+    else rc = pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;  // past the end: last chunk with mass
+    double base = __shfl(excl, rc, kWave);
+    const double err_before = __shfl(err_excl, rc, kWave);
+    // t may lie before the located chunk when it is within the base's error,
+    // and the first-order correction needs rho near 1
+    const bool bad_rho = !bonus && !usep && !(fabs(rho - 1.0) <= kKappa);
+    const bool near_edge = hit && t - base <= err_before + 1e-14 * z;
+    if (bad_rho || near_edge) {
+      rc = 0;
+      base = 0.0;
+    }
+    if (lane == 0) {
+      s_rho = rho;
+      s_t = bad_rho ? ur : (hit || near_edge ? t : INFINITY);
+      s_base = base;
+      s_chunk = rc;
+      s_usep = usep;
+      s_exact_total = bad_rho;
+    }
+  }
+  __shared__ double lds[kSelWaves];
+  __shared__ int s_j, s_jlast;
+  if (threadIdx.x == 0) {
+    s_j = 0x7fffffff;
+    s_jlast = -1;
+  }
+  __syncthreads();
+  const bool usep = s_usep;
+  const double rho = s_rho;
+  double t = s_t;
+  double base = s_base;
+
+  // weights of this lane's kRun consecutive tokens from v0 (0 past chi)
+  auto weights = [&](long v0, long chi, double* wv) {
+    float ep[kRun], eq[kRun];
+    load_run<DT, VEC>(rows.rp, v0, chi, ep);
+    if (bonus || usep) {
+#pragma unroll
+      for (int k = 0; k < kRun; ++k) eq[k] = -INFINITY;
+    } else {
+      load_run<DT, VEC>(rows.rq, v0, chi, eq);
+    }
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+      const double P = wt.P(ep[k]);
+      wv[k] = (bonus || usep) ? P : fmax(P - rho * wt.Q(eq[k]), 0.0);
+    }
+  };
+
+  if (s_exact_total) {  // rare: exact total over every chunk, then t
+    double z = 0.0;
+    for (long r0 = 0; r0 < p.V; r0 += kRound) {
+      double wv[kRun], mine = 0.0;
+      weights(r0 + static_cast<long>(threadIdx.x) * kRun, p.V, wv);
+#pragma unroll
+      for (int k = 0; k < kRun; ++k) mine += wv[k];
+      z += block_sum_n<kSelWaves>(mine, lds);
+    }
+    t = t * z;  // s_t held u in this case
+  }
+
+  // rescan from the chunk holding t until the crossing is found
+  for (int c = s_chunk; c < p.R3; ++c) {
+    const long clo = static_cast<long>(c) * p.ch3;
+    const long chi = min(static_cast<long>(p.V), clo + p.ch3);
+    for (long r0 = clo; r0 < chi; r0 += kRound) {
+      const long v0 = r0 + static_cast<long>(threadIdx.x) * kRun;
+      double wv[kRun], mine = 0.0;
+      weights(v0, chi, wv);
+#pragma unroll
+      for (int k = 0; k < kRun; ++k) mine += wv[k];
+      double total;
+      double run = base + block_exclusive_scan_n<kSelWaves>(mine, lds, &total);
+      int found = -1, lastpos = -1;
+#pragma unroll
+      for (int k = 0; k < kRun; ++k) {
+        if (wv[k] > 0.0) lastpos = static_cast<int>(v0 + k);
+        run += wv[k];
+        if (found < 0 && wv[k] > 0.0 && run > t) found = static_cast<int>(v0 + k);
+      }
+      if (found >= 0) atomicMin(&s_j, found);
+      if (lastpos >= 0) atomicMax(&s_jlast, lastpos);
+      __syncthreads();
+      if (s_j != 0x7fffffff) break;  // uniform: every lane reads the same LDS value
+      base += total;
+    }
+    if (s_j != 0x7fffffff || t == INFINITY) break;  // found, or the past-the-end rule applies
+  }
+  if (threadIdx.x == 0) {
+    *token = s_j != 0x7fffffff ? s_j : s_jlast;
+    *zw_zero = usep && !bonus;
+  }
+}
+
+// ---------------------------------------------------------------- kernels --
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock, 4) void k_exact_chunks(Params p) {
+  const long count = static_cast<long>(p.qcount[0]);
+  for (long item = blockIdx.x; item < count * p.R3; item += gridDim.x) {
+    const long s = p.queue[p.seq0 + item / p.R3];
+    const int r = static_cast<int>(item % p.R3);
+    const SeqRec rec = p.rec[s];
+    const bool bonus = rec.n == p.K;
+    exact_chunk_sums<DT, VEC>(p, decisive_rows<DT>(p, s, rec.n), exact_weight(p, rec), bonus, r,
+                              p.xsum + (s * p.R3 + r) * 5);
+  }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kSelBlock) void k_exact_select(Params p) {
+  const long count = static_cast<long>(p.qcount[0]);
+  for (long e = blockIdx.x; e < count; e += gridDim.x) {
+    const long s = p.queue[p.seq0 + e];
+    const SeqRec rec = p.rec[s];
+    const bool bonus = rec.n == p.K;
+    __syncthreads();  // shared scalars of the previous entry are no longer read
+    int token;
+    bool zw_zero;
+    select_exact<DT, VEC>(p, decisive_rows<DT>(p, s, rec.n), exact_weight(p, rec), bonus, p.xsum + s * p.R3 * 5,
+                          static_cast<double>(p.ur[s]), &token, &zw_zero);
+    if (threadIdx.x == 0) {
+      p.out_tokens[s * (p.K + 1) + rec.n] = token;
+      if (p.out_flags && zw_zero) p.out_flags[s] |= SPECV_FLAG_ZW_ZERO;
+    }
+  }
+}
+
+template <int DT, bool VEC>
+void launch_all(const Params& p, hipStream_t st) {
+  const dim3 block(kBlock);
+  const unsigned ns = static_cast<unsigned>(p.nseq);
+  // grids cover up to kExactSeqs queued sequences in one pass; idle
+  // workgroups exit at once
+  const unsigned nx = ns < kExactSeqs ? ns : kExactSeqs;
+  hipLaunchKernelGGL((k_exact_chunks<DT, VEC>), dim3(nx * p.R3), block, 0, st, p);
+  hipLaunchKernelGGL((k_exact_select<DT, VEC>), dim3(nx), dim3(kSelBlock), 0, st, p);
+}
+
+}  // namespace
+
+hipError_t launch_exact(const Params& p, int dtype, hipStream_t st) {
+  if (dtype == 1) {
+    if (p.vec) launch_all<1, true>(p, st);
+    else launch_all<1, false>(p, st);
+  } else {
+    if (p.vec) launch_all<0, true>(p, st);
+    else launch_all<0, false>(p, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sv

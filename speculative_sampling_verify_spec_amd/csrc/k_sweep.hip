@@ -78,6 +78,7 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   float e[N];
   long lo, hi;
   load_chunk<DT, VEC>(p, sweep_row<DT>(p, row), chunk, e, lo, hi);
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.qcount[0] = 0u;  // the fp64 draw's queue, filled after this kernel
 
   float m = -INFINITY;
 #pragma unroll

@@ -1,0 +1,476 @@
+// The verify step after the row sweep, sampling mode: one workgroup of 1024
+// threads per sequence runs the acceptance scan and then the fast
+// replacement / bonus draw, so no partial result has to cross workgroups.
+//
+// Acceptance.  The 16 waves fold the sweep's per-wave (R, s) partials of the
+// sequence's 2K+1 rows into log2 normalisers (fp64 sums with exact
+// power-of-two rescales; the exponent of the sum exact, its mantissa's log2
+// from v_log_f32).  Lane k of wave 0 evaluates u_k < min(1, p_k(x_k) / q_k(x_k))
+// as an fp64 log2 ratio, and a ballot turns the K answers into n, the index of
+// the first rejection (K if none).  Testing all K at once is exact: the
+// outcome is the first failing test, which is what stopping there yields.
+//
+// Draw.  After n acceptances the token is drawn from w = max(0, p_n - q_n)
+// (n < K) or w = p_K (n == K) by inverse CDF: the smallest v whose running
+// sum C(v) exceeds t = u Z, Z the total.  Only the decisive row (pair) is
+// reread, once.
+//  - Self-normalisation.  With the sweep's normalisers L' as references the
+//    fp32 weights P'(v) = 2^(x c - Wp) and Q'(v) = 2^(y c - Wq - D) are p and
+//    q up to one common factor, and w = max(0, P' - rho Q') / sum P' with
+//    rho = sum P' / sum Q', which is 1 up to the normalisers' error.  The
+//    fast draw takes rho as 1 and adds |sum P' - sum Q'| to its error bound.
+//  - Streaming.  The row is cut into segments of one or more wave iterations
+//    of 64 lanes x U units (16-byte vectors, or single elements on the scalar
+//    path); wave w takes segments w, w + 16, ...  Each lane sums its weights
+//    in fp32 pairwise groups, a DPP wave sum gives the segment's mass (kept in
+//    LDS), and sum P', sum Q' go to fp64 lane totals.
+//  - Select.  Wave 0 scans the segment masses for the segment holding t,
+//    recomputes that segment's weights and finds the token with wave scans in
+//    token order.  The answer stands when t is further from both ends of the
+//    token's interval than a certified bound (fast_bound); otherwise the
+//    sequence joins the queue of the fp64 draw, which also takes the rare
+//    cases of zero residual mass and of t at or past the end.
+#include "sv_device.h"
+#include "specverify.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int kVBlock = 1024;                 // threads per workgroup
+constexpr int kVWaves = kVBlock / kWave;      // 16
+constexpr int kRowsMax = 2 * SPECV_MAX_K + 1;
+constexpr int kRowsPerWave = (kRowsMax + kVWaves - 1) / kVWaves;  // 5 rows per wave at most
+constexpr int kMaxSegs = 1024;                // segment masses kept in LDS
+
+// ------------------------------------------------------------ acceptance --
+// Fold one lane's (R, s) sweep partial into its running pair (ml, sl):
+// exact power-of-two rescales, fp64 sums.
+__device__ inline void fold_partial(float& ml, double& sl, float2 q) {
+  if (q.x == -INFINITY) return;
+  if (q.x > ml) {
+    sl = ml == -INFINITY ? 0.0 : ldexp(sl, static_cast<int>(fmaxf(ml - q.x, -1000.f)));
+    ml = q.x;
+  }
+  sl += ldexp(static_cast<double>(q.y), static_cast<int>(fmaxf(q.x - ml, -1000.f)));
+}
+
+// log2 sum 2^(x c) of a row from the lanes' running pairs (whole wave).  The
+// exponent of the sum is exact (frexp); its mantissa's log2 comes from
+// v_log_f32, good to ~1e-7 absolute, which is all the uses of the normaliser
+// need (the acceptance test's near-tie window is 1e-5 and the draw normalises
+// by its own sums).
+__device__ inline double wave_log2z(float ml, double sl) {
+  const float M = wave_max(ml);
+  const double S = wave_sum(ml == -INFINITY ? 0.0 : ldexp(sl, static_cast<int>(fmaxf(ml - M, -1000.f))));
+  int e;
+  const double m = frexp(S, &e);  // S = m 2^e, m in [1/2, 1)
+  return static_cast<double>(M) + e + __builtin_amdgcn_logf(static_cast<float>(m));
+}
+
+// Runs on the whole workgroup.  Writes the accepted prefix and the padding of
+// out_tokens (slot n is the draw's), out_n, out_logz, and returns the record.
+template <int DT>
+__device__ inline SeqRec accept_scan(const Params& p, long s) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int K = p.K, nrows = 2 * K + 1, np = p.nch1 * kWaves;  // kWaves: the sweep's waves per chunk
+  __shared__ double sL[kRowsMax];  // log2 sum_v 2^(x_v c) of each row
+  __shared__ SeqRec sRec;
+
+  // wave 0 starts the draft-token gathers at once: they do not need the normalisers
+  int xk = 0;
+  bool valid = true;
+  float xp = 0.f, xq = 0.f;
+  if (w == 0 && lane < K) {
+    xk = p.x[s * K + lane];
+    valid = xk >= 0 && xk < p.V;
+    const int xs = valid ? xk : 0;
+    xp = Elt<DT>::at(row_ptr<DT>(p.lp, s * (K + 1) + lane, p.V), xs);
+    xq = Elt<DT>::at(row_ptr<DT>(p.lq, s * K + lane, p.V), xs);
+  }
+
+  // each wave folds its rows; the partial loads of the first 64 per row go out together
+  float ml[kRowsPerWave];
+  double sl[kRowsPerWave];
+  {
+    float2 q[kRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      const int i = w + r * kVWaves;
+      q[r] = (i < nrows && lane < np) ? p.part[(s * nrows + i) * np + lane] : make_float2(-INFINITY, 0.f);
+    }
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      ml[r] = -INFINITY;
+      sl[r] = 0.0;
+      fold_partial(ml[r], sl[r], q[r]);
+    }
+  }
+  for (int j = lane + kWave; j < np; j += kWave)  // long rows: the rest of the partials
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      const int i = w + r * kVWaves;
+      if (i < nrows) fold_partial(ml[r], sl[r], p.part[(s * nrows + i) * np + j]);
+    }
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int i = w + r * kVWaves;
+    if (i >= nrows) break;  // uniform over the wave
+    const double lz2 = wave_log2z(ml[r], sl[r]);
+    if (lane == 0) {
+      sL[i] = lz2;
+      if (p.out_logz) p.out_logz[s * nrows + i] = static_cast<float>(lz2 * M_LN2);
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    bool accept = false;
+    if (lane < K && valid) {
+      const double c = p.c;
+      // log2 p(x) - log2 q(x); -inf - -inf gives NaN, which rejects
+      const double lr = (static_cast<double>(xp) * c - sL[lane]) - (static_cast<double>(xq) * c - sL[K + 1 + lane]);
+      const double thr = lr >= 0.0 ? 1.0 : exp2(lr);
+      accept = static_cast<double>(p.ua[s * K + lane]) < thr;
+    }
+    const uint64_t lim = (K >= 64) ? ~0ull : ((1ull << K) - 1ull);
+    const uint64_t rejected = ~static_cast<uint64_t>(__ballot(accept)) & lim;
+    const int n = rejected ? __ffsll(static_cast<unsigned long long>(rejected)) - 1 : K;
+    const bool bad = __shfl(valid ? 1 : 0, n < K ? n : 0, kWave) == 0 && n < K;
+    if (lane <= K && lane != n) p.out_tokens[s * (K + 1) + lane] = lane < n ? xk : -1;
+    if (lane == 0) {
+      p.out_n[s] = n;
+      SeqRec r;
+      r.n = n;
+      r.flags = bad ? SPECV_FLAG_BAD_DRAFT : 0;
+      r.lzp = sL[n];
+      r.lzq = n < K ? sL[K + 1 + n] : 0.0;
+      p.rec[s] = r;  // read by the fp64 draw if this sequence is queued
+      sRec = r;
+    }
+  }
+  __syncthreads();
+  return sRec;
+}
+
+// ------------------------------------------------------------------ draw --
+// fp32 weights scaled by the common factor 2^Fp: P' = 2^(x c - Wp) and
+// Q' = 2^((y c - Wq) - D), with Wp, Wq = rint(L') whole, Fp, Fq the remaining
+// fractions and D = Fq - Fp, so both references keep the fp32 accuracy of
+// the fractions, not of L'.  A common factor leaves the draw unchanged (it
+// normalises by its own sums), and -inf logits give weights of exactly 0.
+struct FastWeight {
+  float c, Wp, Wq, D;
+  __device__ float P(float x) const { return ex2(fmaf(x, c, -Wp)); }
+  __device__ float Q(float x) const { return ex2(fmaf(x, c, -Wq) - D); }
+};
+
+__device__ inline FastWeight fast_weight(const Params& p, const SeqRec& rec) {
+  FastWeight f;
+  f.c = p.c;
+  const double wp = rint(rec.lzp), wq = rint(rec.lzq);
+  f.Wp = static_cast<float>(wp);
+  f.Wq = static_cast<float>(wq);
+  f.D = static_cast<float>((rec.lzq - wq) - (rec.lzp - wp));
+  return f;
+}
+
+// Segment geometry of a row: units of PV elements, wave iterations of
+// 64 x U units, segments of `iters` iterations, at most kMaxSegs segments.
+template <int DT, bool VEC>
+struct Geometry {
+  static constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
+  static constexpr int U = VEC ? 4 : 8;
+  static constexpr int kIterUnits = kWave * U;
+  long units;
+  int iters, nseg;
+  __device__ explicit Geometry(int V) {
+    units = VEC ? V / PV : V;  // VEC: V is a multiple of PV
+    const long total = (units + kIterUnits - 1) / kIterUnits;
+    iters = static_cast<int>((total + kMaxSegs - 1) / kMaxSegs);
+    nseg = static_cast<int>((total + iters - 1) / iters);
+  }
+};
+
+// One wave iteration at unit `base`: this lane's units base + i*64 + lane
+// (i < U) of the target row (and of the draft row unless BONUS), held raw
+// and widened one unit at a time; units at or past the row's end read as
+// -inf.
+template <int DT, bool VEC, bool BONUS>
+struct Iter {
+  using G = Geometry<DT, VEC>;
+  static constexpr int NR = VEC ? G::U : 1;
+  static constexpr int NS = VEC ? 1 : G::U;
+  uint4 rp[NR], rq[NR];     // vector path: the raw units
+  float xp[NS], xq[NS];     // scalar path: the elements
+  uint32_t live;            // bit i: unit i lies inside the row
+
+  __device__ void load(const void* rowp, const void* rowq, long base, long units) {
+    const int lane = threadIdx.x % kWave;
+    live = 0;
+#pragma unroll
+    for (int i = 0; i < G::U; ++i) {
+      const long u = base + i * kWave + lane;
+      live |= (u < units ? 1u : 0u) << i;
+      if constexpr (VEC) {
+        const long uu = u < units ? u : units - 1;
+        rp[i] = load16(rowp, uu);
+        if constexpr (!BONUS) rq[i] = load16(rowq, uu);
+      } else {
+        xp[i] = load_masked<DT>(rowp, u, units);
+        if constexpr (!BONUS) xq[i] = load_masked<DT>(rowq, u, units);
+      }
+    }
+  }
+  // unit i of the target (Q_ROW false) or draft (true) row
+  template <bool Q_ROW>
+  __device__ void unit(int i, float (&e)[G::PV]) const {
+    if constexpr (VEC) {
+      Elt<DT>::unpack(Q_ROW ? rq[i] : rp[i], e);
+      if (!((live >> i) & 1u)) {
+#pragma unroll
+        for (int k = 0; k < G::PV; ++k) e[k] = -INFINITY;
+      }
+    } else {
+      e[0] = Q_ROW ? xq[i] : xp[i];
+    }
+  }
+};
+
+// Stream the decisive row(s): segment masses into segA, fp64 lane totals of
+// P' and Q'.  Per unit the sums are pairwise in fp32, then pairwise over the
+// lane's U units; the residual mass of a lane is sum P' - sum min(P', Q').
+template <int DT, bool VEC, bool BONUS>
+__device__ inline void stream_row(const void* rp, const void* rq, const FastWeight& wt, const Geometry<DT, VEC>& g,
+                                  float* segA, double& tsp, double& tsq) {
+  using G = Geometry<DT, VEC>;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  for (int j = w; j < g.nseg; j += kVWaves) {
+    float a = 0.f;
+    for (int it = 0; it < g.iters; ++it) {
+      const long base = (static_cast<long>(j) * g.iters + it) * G::kIterUnits;
+      if (base >= g.units) break;  // uniform over the wave
+      Iter<DT, VEC, BONUS> t;
+      t.load(rp, rq, base, g.units);
+      float up[G::U], uq[G::U], um[G::U];
+#pragma unroll
+      for (int i = 0; i < G::U; ++i) {
+        float ep[G::PV], sp[G::PV], sq[G::PV], sm[G::PV];
+        t.template unit<false>(i, ep);
+#pragma unroll
+        for (int k = 0; k < G::PV; ++k) sp[k] = wt.P(ep[k]);
+        if constexpr (!BONUS) {
+          float eq[G::PV];
+          t.template unit<true>(i, eq);
+#pragma unroll
+          for (int k = 0; k < G::PV; ++k) {
+            sq[k] = wt.Q(eq[k]);
+            sm[k] = fminf(sp[k], sq[k]);
+          }
+        }
+#pragma unroll
+        for (int h = G::PV / 2; h > 0; h >>= 1)
+#pragma unroll
+          for (int k = 0; k < h; ++k) {
+            sp[k] += sp[k + h];
+            if constexpr (!BONUS) {
+              sq[k] += sq[k + h];
+              sm[k] += sm[k + h];
+            }
+          }
+        up[i] = sp[0];
+        if constexpr (!BONUS) {
+          uq[i] = sq[0];
+          um[i] = sm[0];
+        } else {
+          uq[i] = um[i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int h = G::U / 2; h > 0; h >>= 1)
+#pragma unroll
+        for (int k = 0; k < h; ++k) {
+          up[k] += up[k + h];
+          uq[k] += uq[k + h];
+          um[k] += um[k + h];
+        }
+      a += BONUS ? up[0] : up[0] - um[0];
+      tsp += up[0];
+      tsq += uq[0];
+    }
+    const float seg = wave_sum_f32(a);
+    if (lane == 0) segA[j] = seg;
+  }
+}
+
+// Certified bound on how far the fast draw's t - C(v) can be from the exact
+// one (C a running sum of the residual, t = u Z), in the units of P'.
+// Per weight, the exponent carries roundings that grow with its size |f|
+// (c's own rounding, the fma, the subtraction of D; a common offset cancels
+// when P' is normalised by its own sum), at most u (3 |f| + 1), and v_exp_f32
+// one ulp (measured <= 0.78), so the relative error is <= u (2.7 + 2.08 |f|),
+// u = 2^-24.  Summed over a row, sum P' |f| <= sum P' (log2 V + 1) (an entropy
+// bound).  The fp32 sums (within a unit, over a lane's units, over the
+// segment's iterations, the DPP wave sum), the residual's subtraction and the
+// rescan's rounding add at most (13 + iters) u (SP + SQ).  So one running sum is off by
+// R <= u (16 + iters + 2.1 (log2 V + 1)) (SP + SQ), and t by as much.  Taking
+// rho as 1 moves each residual weight by at most |rho - 1| Q', so a running
+// sum and Z by at most |SP - SQ|.  Both errors enter twice (t and C), and the
+// whole carries a safety factor of 2.
+__device__ inline double fast_bound(double SP, double SQ, int V, int iters, bool bonus) {
+  const double u = 0x1p-24;
+  const double R = u * (16.0 + iters + 2.1 * (log2(static_cast<double>(V)) + 1.0)) * (SP + SQ);
+  return 2.0 * (2.0 * R + (bonus ? 0.0 : 2.0 * fabs(SP - SQ)));
+}
+
+// Wave 0: find the token of segment j whose running sum first exceeds t,
+// given the mass `base` of the segments before it.  Weights are recomputed
+// exactly as in stream_row; token order within an iteration is (unit i,
+// lane, element k).
+// Returns false when rounding leaves the crossing outside the segment.
+template <int DT, bool VEC, bool BONUS>
+__device__ inline bool rescan_segment(const void* rp, const void* rq, const FastWeight& wt,
+                                      const Geometry<DT, VEC>& g, int j, double base, double t,
+                                      int* token, double* lo, double* hi) {
+  using G = Geometry<DT, VEC>;
+  const int lane = threadIdx.x % kWave;
+  for (int it = 0; it < g.iters; ++it) {
+    const long ubase = (static_cast<long>(j) * g.iters + it) * G::kIterUnits;
+    if (ubase >= g.units) break;
+    Iter<DT, VEC, BONUS> tl;
+    tl.load(rp, rq, ubase, g.units);
+#pragma unroll
+    for (int i = 0; i < G::U; ++i) {
+      float wv[G::PV];
+      {
+        float ep[G::PV];
+        tl.template unit<false>(i, ep);
+#pragma unroll
+        for (int k = 0; k < G::PV; ++k) wv[k] = wt.P(ep[k]);
+        if constexpr (!BONUS) {
+          float eq[G::PV];
+          tl.template unit<true>(i, eq);
+#pragma unroll
+          for (int k = 0; k < G::PV; ++k) wv[k] = fmaxf(wv[k] - wt.Q(eq[k]), 0.f);
+        }
+      }
+      double mine = 0.0;
+#pragma unroll
+      for (int k = 0; k < G::PV; ++k) mine += wv[k];
+      const double inc = wave_inclusive_scan(mine);
+      const double total = __shfl(inc, kWave - 1, kWave);
+      const uint64_t hit = __ballot(base + inc > t);
+      if (hit) {
+        const int L = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        int tk = -1;
+        double tlo = 0.0, thi = 0.0;
+        if (lane == L) {
+          double run = base + inc - mine;
+#pragma unroll
+          for (int k = 0; k < G::PV; ++k) {
+            const double before = run;
+            run += wv[k];
+            if (tk < 0 && wv[k] > 0.f && run > t) {
+              tk = k;
+              tlo = before;
+              thi = run;
+            }
+          }
+        }
+        tk = __shfl(tk, L, kWave);
+        if (tk < 0) return false;  // the lane's sum crossed t only by rounding
+        *token = static_cast<int>((ubase + i * kWave + L) * G::PV + tk);
+        *lo = __shfl(tlo, L, kWave);
+        *hi = __shfl(thi, L, kWave);
+        return true;
+      }
+      base += total;
+    }
+  }
+  return false;
+}
+
+template <int DT, bool VEC, bool BONUS>
+__device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec) {
+  using G = Geometry<DT, VEC>;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const G g(p.V);
+  const FastWeight wt = fast_weight(p, rec);
+  const void* rp = row_ptr<DT>(p.lp, s * (p.K + 1) + rec.n, p.V);
+  const void* rq = BONUS ? nullptr : row_ptr<DT>(p.lq, s * p.K + rec.n, p.V);
+  __shared__ float segA[kMaxSegs];
+  __shared__ double lds[kVWaves];
+
+  double tsp = 0.0, tsq = 0.0;
+  stream_row<DT, VEC, BONUS>(rp, rq, wt, g, segA, tsp, tsq);
+  const double SP = block_sum_n<kVWaves>(tsp, lds);  // its barriers also publish segA
+  const double SQ = BONUS ? 0.0 : block_sum_n<kVWaves>(tsq, lds);
+  if (w != 0) return;
+
+  // segments per lane, consecutive; wave scan of the lanes' masses
+  const int per = (g.nseg + kWave - 1) / kWave;
+  double mine = 0.0;
+  for (int k = 0; k < per; ++k) {
+    const int j = lane * per + k;
+    if (j < g.nseg) mine += segA[j];
+  }
+  const double inc = wave_inclusive_scan(mine);
+  const double Z = __shfl(inc, kWave - 1, kWave);
+  const double t = static_cast<double>(p.ur[s]) * Z;
+  const uint64_t hit = __ballot(inc > t);
+  bool certain = false;
+  int token = -1;
+  if (Z > 0.0 && hit) {
+    const int L = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+    int jseg = -1;
+    double jbase = 0.0;
+    if (lane == L) {
+      double run = inc - mine;
+      for (int k = 0; k < per && jseg < 0; ++k) {
+        const int j = lane * per + k;
+        if (j < g.nseg) {
+          if (run + segA[j] > t) jseg = j;
+          else run += segA[j];
+        }
+      }
+      jbase = run;
+    }
+    jseg = __shfl(jseg, L, kWave);
+    jbase = __shfl(jbase, L, kWave);
+    double lo = 0.0, hi = 0.0;
+    if (jseg >= 0 && rescan_segment<DT, VEC, BONUS>(rp, rq, wt, g, jseg, jbase, t, &token, &lo, &hi))
+      certain = fmin(t - lo, hi - t) > fast_bound(SP, SQ, p.V, g.iters, BONUS);
+  }
+  if (lane == 0) {
+    if (p.out_flags) p.out_flags[s] = rec.flags;
+    if (certain) {
+      p.out_tokens[s * (p.K + 1) + rec.n] = token;
+    } else {
+      const uint32_t slot = atomicAdd(&p.qcount[0], 1u);
+      p.queue[p.seq0 + slot] = static_cast<int32_t>(s);
+    }
+  }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kVBlock) void k_verify(Params p) {
+  const long s = p.seq0 + blockIdx.x;
+  const SeqRec rec = accept_scan<DT>(p, s);
+  if (rec.n == p.K) fast_draw<DT, VEC, true>(p, s, rec);
+  else fast_draw<DT, VEC, false>(p, s, rec);
+}
+
+}  // namespace
+
+hipError_t launch_verify(const Params& p, int dtype, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(p.nseq)), block(kVBlock);
+  if (dtype == 1) {
+    if (p.vec) hipLaunchKernelGGL((k_verify<1, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((k_verify<1, false>), grid, block, 0, st, p);
+  } else {
+    if (p.vec) hipLaunchKernelGGL((k_verify<0, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((k_verify<0, false>), grid, block, 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sv

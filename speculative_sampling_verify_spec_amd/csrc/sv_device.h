@@ -109,6 +109,24 @@ __device__ inline double wave_sum(double v) {
   return v;
 }
 
+// fp32 sum over a whole wave (all 64 lanes active) by DPP: butterflies within
+// rows of 16 lanes, then two row broadcasts; fixed order, so deterministic.
+// Every lane gets the total (lane 63's value, read as a scalar).
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+__device__ inline float wave_sum_f32(float v) {
+  v += dpp_f32<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141, 0xf>(v);  // row_half_mirror
+  v += dpp_f32<0x140, 0xf>(v);  // row_mirror: every lane holds its row's sum
+  v += dpp_f32<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f32<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3: lane 63 holds the total
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Combine (max, sum-scaled-to-max) pairs where sum = sum 2^((x - max) c).
 __device__ inline void lse_merge(float& m, float& s, float m2, float s2, float c) {
   const float M = fmaxf(m, m2);
@@ -141,8 +159,10 @@ __device__ inline void wave_argmax(float& v, int& i) {
   }
 }
 
-// Workgroup-wide sum of one double per thread; every thread gets the total.
-__device__ inline double block_sum(double v, double* lds /* >= kWaves */) {
+// Workgroup-wide sum of one double per thread over NW waves; every thread
+// gets the total.
+template <int NW>
+__device__ inline double block_sum_n(double v, double* lds /* >= NW */) {
   v = wave_sum(v);
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   __syncthreads();
@@ -150,9 +170,11 @@ __device__ inline double block_sum(double v, double* lds /* >= kWaves */) {
   __syncthreads();
   double t = 0.0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) t += lds[i];
+  for (int i = 0; i < NW; ++i) t += lds[i];
   return t;
 }
+
+__device__ inline double block_sum(double v, double* lds /* >= kWaves */) { return block_sum_n<kWaves>(v, lds); }
 
 __device__ inline float block_max(float v, float* lds /* >= kWaves */) {
   v = wave_max(v);
@@ -177,9 +199,11 @@ __device__ inline double wave_inclusive_scan(double v) {
   return v;
 }
 
-// Exclusive prefix sum of one double per thread over the workgroup, in
-// thread order.  Returns the exclusive prefix; *total gets the block total.
-__device__ inline double block_exclusive_scan(double v, double* lds /* >= kWaves */, double* total) {
+// Exclusive prefix sum of one double per thread over a workgroup of NW
+// waves, in thread order.  Returns the exclusive prefix; *total gets the
+// block total.
+template <int NW>
+__device__ inline double block_exclusive_scan_n(double v, double* lds /* >= NW */, double* total) {
   const double inc = wave_inclusive_scan(v);
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   double excl = __shfl_up(inc, 1, kWave);
@@ -189,7 +213,7 @@ __device__ inline double block_exclusive_scan(double v, double* lds /* >= kWaves
   __syncthreads();
   double before = 0.0, all = 0.0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     if (i < w) before += lds[i];
     all += lds[i];
   }

@@ -10,7 +10,7 @@ namespace sv {
 constexpr int kBlock = 256;   // threads per workgroup in every kernel
 constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kWaves = kBlock / kWave;
-constexpr int kMaxDrawChunks = 64;    // draw chunks per row: one wave combines them
+constexpr int kMaxDrawChunks = 64;    // fp64 draw chunks per row: one wave combines them
 
 // Elements one lane of the row sweep holds: six 16-byte units on the vector
 // path, sixteen single elements on the scalar path.
@@ -19,7 +19,7 @@ constexpr int kSweepElems() {
   return VEC ? 6 * (DT == 1 ? 8 : 4) : 16;
 }
 
-// Per-sequence record written by the acceptance scan and read by the draw.
+// Per-sequence record written by the acceptance scan and read by the fp64 draw.
 struct SeqRec {
   int32_t n;       // accepted draft tokens
   int32_t flags;   // SPECV_FLAG_* set so far
@@ -45,19 +45,18 @@ struct Params {
   // workspace
   float2* part;              // [rows][nch1][kWaves] (R, s) sweep partials, or (max, index bits) in greedy mode
   SeqRec* rec;               // [B]
-  double* csum;              // [B][R3][5] fast draw chunk sums
   double* xsum;              // [B][R3][5] exact draw chunk sums (queued sequences)
   uint32_t* qcount;          // [1] sequences queued for the exact draw
   int32_t* queue;            // [B] their ids (from the first sequence of the launch on)
   int nch1, ch1;             // sweep chunks per row, elements per sweep chunk (at most)
   int cq, cr;                // sweep chunk c spans c*cq + min(c, cr) .. + cq + (c < cr) units
-  int R3, ch3;               // draw chunks per row, elements per draw chunk
+  int R3, ch3;               // fp64 draw chunks per row, elements per chunk
   int seq0, nseq;            // the sequences a launch covers
 };
 
 // Workspace layout (byte offsets), shared by spec_verify_workspace_size and the launcher.
 struct Layout {
-  size_t part, rec, csum, xsum, queue, qcount, total;
+  size_t part, rec, xsum, queue, qcount, total;
   int nch1, ch1, cq, cr, R3, ch3;
 };
 
@@ -66,8 +65,8 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy);
 // Launchers (one per kernel), defined next to their kernels.
 hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
-hipError_t launch_accept_scan(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_verify(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_exact(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_greedy_scan(const Params& p, hipStream_t s);
-hipError_t launch_draw(const Params& p, int dtype, hipStream_t s);
 
 }  // namespace sv
