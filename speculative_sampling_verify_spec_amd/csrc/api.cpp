@@ -40,10 +40,10 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
     L.total = off;
     return L;
   }
-  // fp64 draw chunks: multiples of 2048 elements, at most kMaxDrawChunks per row
-  long ch = 4096;
+  // fp64 draw chunks: multiples of 1024 elements, at most kMaxDrawChunks per row
+  long ch = 1024;
   const long need = (static_cast<long>(V) + kMaxDrawChunks - 1) / kMaxDrawChunks;
-  if (need > ch) ch = (need + 2047) / 2048 * 2048;
+  if (need > ch) ch = (need + 1023) / 1024 * 1024;
   L.ch3 = static_cast<int>(ch);
   L.R3 = static_cast<int>((V + ch - 1) / ch);
   L.rec = off;

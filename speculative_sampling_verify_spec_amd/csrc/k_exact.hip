@@ -7,14 +7,14 @@
 // w = max(0, P - rho Q) / sum P with rho = sum P / sum Q.
 //
 // Two kernels walk the queue the fast draw filled:
-//   exact_chunks (queued sequences x chunks of ch3 tokens): per chunk
+//   exact_chunks (queued sequences x chunks of ch3 >= 1024 tokens): per chunk
 //        sum P, sum Q, A = sum max(0, P - Q), G = sum_{P > Q} Q and
 //        H = sum_{near flip} Q, the Q-mass within a relative kKappa of P = Q.
 //        The chunk's residual mass at the exact rho is A - (rho - 1) G up to
 //        the mass of tokens whose sign flips, which is at most |rho - 1| H.
 //   exact_select (one workgroup per queued sequence): rho and the corrected
 //        chunk sums give Z and the chunk holding t; that chunk is rescanned
-//        (lane-contiguous runs, fp64 scan over 512 threads) with the exact
+//        (lane-contiguous runs, fp64 scan over 128 threads) with the exact
 //        rho.  When t may lie before the located chunk (within the
 //        corrections' error) the rescan starts from the first chunk; when rho
 //        leaves the linearisation window the total is recomputed exactly
@@ -30,10 +30,10 @@ namespace sv {
 
 namespace {
 
-constexpr int kSelBlock = 512;                   // threads of the select workgroup
-constexpr int kSelWaves = kSelBlock / kWave;
+constexpr int kXBlock = 128;                     // threads of every workgroup here
+constexpr int kXWaves = kXBlock / kWave;
 constexpr int kRun = 8;                          // elements per lane per rescan round (a whole bf16 vector)
-constexpr int kRound = kSelBlock * kRun;         // 4096 elements per round (one chunk)
+constexpr int kRound = kXBlock * kRun;           // 1024 elements per round (the smallest chunk)
 constexpr double kKappa = 1e-4;                  // near-flip window, relative to Q
 constexpr unsigned kExactSeqs = 32;              // queued sequences the kernels cover per pass
 
@@ -77,15 +77,15 @@ __device__ inline void exact_chunk_sums(const Params& p, const Rows<DT>& rows, c
   const long lo = static_cast<long>(r) * p.ch3;
   const long hi = min(static_cast<long>(p.V), lo + p.ch3);
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  constexpr int U = VEC ? 2 : 8;
+  constexpr int U = 8 / PV;  // eight elements per lane per iteration
   const long ulo = lo / PV, uhi = hi / PV;  // VEC: lo and hi are multiples of PV
   double acc[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
-  for (long r0 = ulo; r0 < uhi; r0 += static_cast<long>(kBlock) * U) {
+  for (long r0 = ulo; r0 < uhi; r0 += static_cast<long>(kXBlock) * U) {
     uint4 rp[VEC ? U : 1], rq[VEC ? U : 1];
     float sp_[VEC ? 1 : U], sq_[VEC ? 1 : U];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-      const long u = r0 + threadIdx.x + static_cast<long>(i) * kBlock;
+      const long u = r0 + threadIdx.x + static_cast<long>(i) * kXBlock;
       if constexpr (VEC) {
         const long uu = u < uhi ? u : uhi - 1;
         rp[i] = load16(rows.rp, uu);
@@ -101,11 +101,11 @@ __device__ inline void exact_chunk_sums(const Params& p, const Rows<DT>& rows, c
       if constexpr (VEC) {
         Elt<DT>::unpack(rp[i], ep);
         if (!bonus) Elt<DT>::unpack(rq[i], eq);
-        if (bonus || r0 + threadIdx.x + static_cast<long>(i) * kBlock >= uhi) {
+        if (bonus || r0 + threadIdx.x + static_cast<long>(i) * kXBlock >= uhi) {
 #pragma unroll
           for (int k = 0; k < PV; ++k) eq[k] = -INFINITY;
         }
-        if (r0 + threadIdx.x + static_cast<long>(i) * kBlock >= uhi) {
+        if (r0 + threadIdx.x + static_cast<long>(i) * kXBlock >= uhi) {
 #pragma unroll
           for (int k = 0; k < PV; ++k) ep[k] = -INFINITY;
         }
@@ -132,7 +132,7 @@ __device__ inline void exact_chunk_sums(const Params& p, const Rows<DT>& rows, c
       acc[4] += h;
     }
   }
-  __shared__ double lds[kWaves][5];
+  __shared__ double lds[kXWaves][5];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
 #pragma unroll
   for (int k = 0; k < 5; ++k) acc[k] = wave_sum(acc[k]);
@@ -145,7 +145,7 @@ __device__ inline void exact_chunk_sums(const Params& p, const Rows<DT>& rows, c
   if (threadIdx.x < 5) {
     double t = 0.0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) t += lds[i][threadIdx.x];
+    for (int i = 0; i < kXWaves; ++i) t += lds[i][threadIdx.x];
     if (!bonus || threadIdx.x == 0) out[threadIdx.x] = t;
   }
 }
@@ -188,37 +188,84 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
   __shared__ double s_base;
   __shared__ int s_chunk, s_usep, s_exact_total;
   if (threadIdx.x < kWave) {
-    const bool have = lane < p.R3;
-    const double* cs = cs_base + (have ? lane : 0) * 5;
-    const double sp = have ? cs[0] : 0.0;
-    const double SP = wave_sum(sp);
-    double v = sp, rho = 1.0, err = 0.0;
+    // lane l owns chunks l*per .. l*per + per - 1
+    const int per = (p.R3 + kWave - 1) / kWave;
+    auto cs = [&](int k, int f) {
+      const int c = lane * per + k;
+      return c < p.R3 ? cs_base[c * 5 + f] : 0.0;
+    };
+    double sp_l = 0.0, sq_l = 0.0;
+    for (int k = 0; k < per; ++k) {
+      sp_l += cs(k, 0);
+      if (!bonus) sq_l += cs(k, 1);
+    }
+    const double SP = wave_sum(sp_l);
+    double rho = 1.0;
     int usep = 1;
+    // chunk k's mass: the residual corrected to first order in rho - 1 (and
+    // its error bound), or p's mass for a bonus or zero-residual draw
+    auto mass = [&](int k, bool use_p) {
+      return use_p ? cs(k, 0) : fmax(cs(k, 2) - (rho - 1.0) * cs(k, 3), 0.0);
+    };
+    auto merr = [&](int k, bool use_p) { return use_p ? 0.0 : fabs(rho - 1.0) * cs(k, 4); };
     if (!bonus) {
-      const double sq = have ? cs[1] : 0.0, a = have ? cs[2] : 0.0;
-      const double g = have ? cs[3] : 0.0, h = have ? cs[4] : 0.0;
-      const double SQ = wave_sum(sq);
+      const double SQ = wave_sum(sq_l);
       rho = SP / SQ;
-      // first-order correction to the exact rho, with its error bound
-      const double corrected = fmax(a - (rho - 1.0) * g, 0.0);
-      const double Z = wave_sum(corrected);
-      usep = !(Z > 0.0);  // p == q to rounding: draw from p_n instead
-      v = usep ? sp : corrected;
-      err = usep ? 0.0 : fabs(rho - 1.0) * h;
+      double z_l = 0.0;
+      for (int k = 0; k < per; ++k) z_l += mass(k, false);
+      usep = !(wave_sum(z_l) > 0.0);  // p == q to rounding: draw from p_n instead
+    }
+    const bool use_p = bonus || usep;
+    double v = 0.0, err = 0.0;
+    for (int k = 0; k < per; ++k) {
+      v += mass(k, use_p);
+      err += merr(k, use_p);
     }
     const double inc = wave_inclusive_scan(v);
     const double err_inc = wave_inclusive_scan(err);
-    double excl = __shfl_up(inc, 1, kWave), err_excl = __shfl_up(err_inc, 1, kWave);
-    if (lane == 0) excl = err_excl = 0.0;
     const double z = __shfl(inc, kWave - 1, kWave);
     const double t = ur * z;
-    const uint64_t hit = __ballot(have && inc > t);
-    const uint64_t pos = __ballot(have && v > 0.0);
-    int rc;
-    if (hit) rc = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-    else rc = pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;  // past the end: last chunk with mass
-    double base = __shfl(excl, rc, kWave);
-    const double err_before = __shfl(err_excl, rc, kWave);
+    const uint64_t hit = __ballot(inc > t);
+    const uint64_t pos = __ballot(v > 0.0);
+    // the lane holding the crossing (or, past the end, the last mass) finds its chunk
+    const int L = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1
+                      : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
+    int rc = 0;
+    double base = 0.0, err_before = 0.0;
+    if (lane == L) {
+      // the chunk where the running mass passes t; if rounding finds none in
+      // this lane (or past the end), the lane's last chunk with mass
+      double run = inc - v, erun = err_inc - err;
+      int last = lane * per;
+      double run_last = run, erun_last = erun;
+      rc = -1;
+      for (int k = 0; k < per; ++k) {
+        const int c = lane * per + k;
+        if (c >= p.R3) break;
+        const double m = mass(k, use_p);
+        if (hit && run + m > t) {
+          rc = c;
+          break;
+        }
+        if (m > 0.0) {
+          last = c;
+          run_last = run;
+          erun_last = erun;
+        }
+        run += m;
+        erun += merr(k, use_p);
+      }
+      if (rc < 0) {
+        rc = last;
+        run = run_last;
+        erun = erun_last;
+      }
+      base = run;
+      err_before = erun;
+    }
+    rc = __shfl(rc, L, kWave);
+    base = __shfl(base, L, kWave);
+    err_before = __shfl(err_before, L, kWave);
     // t may lie before the located chunk when it is within the base's error,
     // and the first-order correction needs rho near 1
     const bool bad_rho = !bonus && !usep && !(fabs(rho - 1.0) <= kKappa);
@@ -236,7 +283,7 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
       s_exact_total = bad_rho;
     }
   }
-  __shared__ double lds[kSelWaves];
+  __shared__ double lds[kXWaves];
   __shared__ int s_j, s_jlast;
   if (threadIdx.x == 0) {
     s_j = 0x7fffffff;
@@ -272,7 +319,7 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
       weights(r0 + static_cast<long>(threadIdx.x) * kRun, p.V, wv);
 #pragma unroll
       for (int k = 0; k < kRun; ++k) mine += wv[k];
-      z += block_sum_n<kSelWaves>(mine, lds);
+      z += block_sum_n<kXWaves>(mine, lds);
     }
     t = t * z;  // s_t held u in this case
   }
@@ -288,7 +335,7 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
 #pragma unroll
       for (int k = 0; k < kRun; ++k) mine += wv[k];
       double total;
-      double run = base + block_exclusive_scan_n<kSelWaves>(mine, lds, &total);
+      double run = base + block_exclusive_scan_n<kXWaves>(mine, lds, &total);
       int found = -1, lastpos = -1;
 #pragma unroll
       for (int k = 0; k < kRun; ++k) {
@@ -296,8 +343,13 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
         run += wv[k];
         if (found < 0 && wv[k] > 0.0 && run > t) found = static_cast<int>(v0 + k);
       }
-      if (found >= 0) atomicMin(&s_j, found);
-      if (lastpos >= 0) atomicMax(&s_jlast, lastpos);
+      // one LDS atomic per wave: the wave's first crossing and last positive weight
+      const int fw = wave_min_i32(found >= 0 ? found : 0x7fffffff);
+      const int lw = wave_max_i32(lastpos);
+      if (lane == 0) {
+        if (fw != 0x7fffffff) atomicMin(&s_j, fw);
+        if (lw >= 0) atomicMax(&s_jlast, lw);
+      }
       __syncthreads();
       if (s_j != 0x7fffffff) break;  // uniform: every lane reads the same LDS value
       base += total;
@@ -312,7 +364,7 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
 
 // ---------------------------------------------------------------- kernels --
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock, 4) void k_exact_chunks(Params p) {
+__global__ __launch_bounds__(kXBlock) void k_exact_chunks(Params p) {
   const long count = static_cast<long>(p.qcount[0]);
   for (long item = blockIdx.x; item < count * p.R3; item += gridDim.x) {
     const long s = p.queue[p.seq0 + item / p.R3];
@@ -325,7 +377,7 @@ __global__ __launch_bounds__(kBlock, 4) void k_exact_chunks(Params p) {
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kSelBlock) void k_exact_select(Params p) {
+__global__ __launch_bounds__(kXBlock) void k_exact_select(Params p) {
   const long count = static_cast<long>(p.qcount[0]);
   for (long e = blockIdx.x; e < count; e += gridDim.x) {
     const long s = p.queue[p.seq0 + e];
@@ -345,13 +397,13 @@ __global__ __launch_bounds__(kSelBlock) void k_exact_select(Params p) {
 
 template <int DT, bool VEC>
 void launch_all(const Params& p, hipStream_t st) {
-  const dim3 block(kBlock);
+  const dim3 block(kXBlock);
   const unsigned ns = static_cast<unsigned>(p.nseq);
   // grids cover up to kExactSeqs queued sequences in one pass; idle
   // workgroups exit at once
   const unsigned nx = ns < kExactSeqs ? ns : kExactSeqs;
   hipLaunchKernelGGL((k_exact_chunks<DT, VEC>), dim3(nx * p.R3), block, 0, st, p);
-  hipLaunchKernelGGL((k_exact_select<DT, VEC>), dim3(nx), dim3(kSelBlock), 0, st, p);
+  hipLaunchKernelGGL((k_exact_select<DT, VEC>), dim3(nx), block, 0, st, p);
 }
 
 }  // namespace

@@ -37,30 +37,38 @@ __device__ inline const void* sweep_row(const Params& p, uint32_t row) {
 }
 
 // This lane's elements of chunk `chunk` of a row (units of 16 bytes when VEC,
-// single elements otherwise), loaded without branches; elements past the
-// chunk read as -inf.  Returns the chunk's unit range.
+// single elements otherwise), loaded without branches.  Bit i of `live` says
+// whether slot i lies inside the chunk.  VEC: units are addressed from the
+// chunk's (scalar) base with 32-bit lane offsets, and a slot past the chunk's
+// end reads the chunk's last unit again (real values of the same chunk, so
+// they leave its maximum unchanged; sums must skip them).  Scalar path:
+// elements past the end read as -inf.  Returns the chunk's unit range.
 template <int DT, bool VEC>
 __device__ inline void load_chunk(const Params& p, const void* r, uint32_t chunk, float (&e)[kSweepElems<DT, VEC>()],
-                                  long& lo, long& hi) {
+                                  uint32_t& live, long& lo, long& hi) {
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
   constexpr int IT = kSweepElems<DT, VEC>() / PV;
   lo = static_cast<long>(chunk) * p.cq + min(static_cast<int>(chunk), p.cr);
   hi = lo + p.cq + (static_cast<int>(chunk) < p.cr ? 1 : 0);
+  const uint32_t n = static_cast<uint32_t>(hi - lo);  // cq or cq + 1 units
+  live = 0;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const uint32_t u = threadIdx.x + i * kBlock;
+    // slots that every chunk fills (a test uniform over the launch) are live everywhere
+    live |= (((i + 1) * kBlock <= p.cq || u < n) ? 1u : 0u) << i;
+  }
   if constexpr (VEC) {
-    uint4 raw[IT];
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4* base = static_cast<const u32x4*>(r) + lo;
+    u32x4 raw[IT];
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const long u = lo + threadIdx.x + static_cast<long>(i) * kBlock;
-      raw[i] = load16_nt(r, u < hi ? u : hi - 1);
+      const uint32_t u = threadIdx.x + i * kBlock;
+      raw[i] = __builtin_nontemporal_load(base + ((i + 1) * kBlock <= p.cq ? u : min(u, n - 1)));
     }
 #pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      Elt<DT>::unpack(raw[i], &e[i * PV]);
-      if (lo + threadIdx.x + static_cast<long>(i) * kBlock >= hi) {
-#pragma unroll
-        for (int k = 0; k < PV; ++k) e[i * PV + k] = -INFINITY;
-      }
-    }
+    for (int i = 0; i < IT; ++i) Elt<DT>::unpack(make_uint4(raw[i].x, raw[i].y, raw[i].z, raw[i].w), &e[i * PV]);
   } else {
 #pragma unroll
     for (int i = 0; i < IT; ++i) e[i] = load_masked<DT>(r, lo + threadIdx.x + static_cast<long>(i) * kBlock, hi);
@@ -76,8 +84,9 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   const uint32_t row = static_cast<uint32_t>(p.seq0) * (2u * p.K + 1u) + local;
   const float c = p.c;
   float e[N];
+  uint32_t live;
   long lo, hi;
-  load_chunk<DT, VEC>(p, sweep_row<DT>(p, row), chunk, e, lo, hi);
+  load_chunk<DT, VEC>(p, sweep_row<DT>(p, row), chunk, e, live, lo, hi);
   if (blockIdx.x == 0 && threadIdx.x == 0) p.qcount[0] = 0u;  // the fp64 draw's queue, filled after this kernel
 
   float m = -INFINITY;
@@ -96,7 +105,7 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
       for (int w = PV / 2; w > 0; w >>= 1)
 #pragma unroll
         for (int k = 0; k < w; ++k) t[k] += t[k + w];
-      s += t[0];
+      s += ((live >> i) & 1u) ? t[0] : 0.f;
     }
   }
 
@@ -116,19 +125,22 @@ __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
   const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
   const uint32_t row = static_cast<uint32_t>(p.seq0) * (p.K + 1u) + local;
   float e[N];
+  uint32_t live;
   long lo, hi;
-  load_chunk<DT, VEC>(p, row_ptr<DT>(p.lp, row, p.V), chunk, e, lo, hi);
-  // a lane visits its elements in increasing index order, so a strict
-  // comparison keeps the lowest index among equal values
+  load_chunk<DT, VEC>(p, row_ptr<DT>(p.lp, row, p.V), chunk, e, live, lo, hi);
+  // the lane's largest value, then the lowest index holding it (a backward
+  // pass of selects over the lane's elements, which it visits in increasing
+  // index order); repeated tail units carry their real index
   float bv = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < N; ++k) bv = fmaxf(bv, e[k]);
   int bi = 0x7fffffff;
 #pragma unroll
-  for (int i = 0; i < N / PV; ++i) {
+  for (int i = N / PV - 1; i >= 0; --i) {
     const long u = lo + threadIdx.x + static_cast<long>(i) * kBlock;
-    if (u < hi) {
+    const long ur = ((live >> i) & 1u) ? u : hi - 1;  // the unit actually read
 #pragma unroll
-      for (int k = 0; k < PV; ++k) argmax_merge(bv, bi, e[i * PV + k], static_cast<int>(u * PV + k));
-    }
+    for (int k = PV - 1; k >= 0; --k) bi = e[i * PV + k] == bv ? static_cast<int>(ur * PV + k) : bi;
   }
   wave_argmax(bv, bi);
   if (threadIdx.x % kWave == 0)

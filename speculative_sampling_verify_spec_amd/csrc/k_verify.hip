@@ -193,8 +193,11 @@ struct Geometry {
 
 // One wave iteration at unit `base`: this lane's units base + i*64 + lane
 // (i < U) of the target row (and of the draft row unless BONUS), held raw
-// and widened one unit at a time; units at or past the row's end read as
-// -inf.
+// and widened one unit at a time.  Bit i of `live` says whether unit i lies
+// inside the row.  Vector path: units are addressed from the iteration's
+// scalar base with 32-bit offsets, and a unit past the row's end reads the
+// row's last unit again (its sums must be skipped, or its elements masked).
+// Scalar path: elements past the end read as -inf.
 template <int DT, bool VEC, bool BONUS>
 struct Iter {
   using G = Geometry<DT, VEC>;
@@ -206,27 +209,36 @@ struct Iter {
 
   __device__ void load(const void* rowp, const void* rowq, long base, long units) {
     const int lane = threadIdx.x % kWave;
+    const long rem = units - base;  // > 0
     live = 0;
 #pragma unroll
-    for (int i = 0; i < G::U; ++i) {
-      const long u = base + i * kWave + lane;
-      live |= (u < units ? 1u : 0u) << i;
-      if constexpr (VEC) {
-        const long uu = u < units ? u : units - 1;
-        rp[i] = load16(rowp, uu);
-        if constexpr (!BONUS) rq[i] = load16(rowq, uu);
-      } else {
-        xp[i] = load_masked<DT>(rowp, u, units);
-        if constexpr (!BONUS) xq[i] = load_masked<DT>(rowq, u, units);
+    for (int i = 0; i < G::U; ++i) live |= ((i * kWave + lane) < rem ? 1u : 0u) << i;
+    if constexpr (VEC) {
+      const uint4* bp = static_cast<const uint4*>(rowp) + base;
+      const uint4* bq = BONUS ? nullptr : static_cast<const uint4*>(rowq) + base;
+      const uint32_t last = static_cast<uint32_t>(rem < G::kIterUnits ? rem - 1 : G::kIterUnits - 1);
+#pragma unroll
+      for (int i = 0; i < G::U; ++i) {
+        const uint32_t off = min(static_cast<uint32_t>(i * kWave + lane), last);
+        rp[i] = bp[off];
+        if constexpr (!BONUS) rq[i] = bq[off];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::U; ++i) {
+        xp[i] = load_masked<DT>(rowp, base + i * kWave + lane, units);
+        if constexpr (!BONUS) xq[i] = load_masked<DT>(rowq, base + i * kWave + lane, units);
       }
     }
   }
-  // unit i of the target (Q_ROW false) or draft (true) row
-  template <bool Q_ROW>
+  __device__ bool is_live(int i) const { return (live >> i) & 1u; }
+  // unit i of the target (Q_ROW false) or draft (true) row; MASK: -inf when
+  // the unit lies past the row's end (otherwise it may repeat the last unit)
+  template <bool Q_ROW, bool MASK>
   __device__ void unit(int i, float (&e)[G::PV]) const {
     if constexpr (VEC) {
       Elt<DT>::unpack(Q_ROW ? rq[i] : rp[i], e);
-      if (!((live >> i) & 1u)) {
+      if (MASK && !is_live(i)) {
 #pragma unroll
         for (int k = 0; k < G::PV; ++k) e[k] = -INFINITY;
       }
@@ -255,12 +267,12 @@ __device__ inline void stream_row(const void* rp, const void* rq, const FastWeig
 #pragma unroll
       for (int i = 0; i < G::U; ++i) {
         float ep[G::PV], sp[G::PV], sq[G::PV], sm[G::PV];
-        t.template unit<false>(i, ep);
+        t.template unit<false, false>(i, ep);
 #pragma unroll
         for (int k = 0; k < G::PV; ++k) sp[k] = wt.P(ep[k]);
         if constexpr (!BONUS) {
           float eq[G::PV];
-          t.template unit<true>(i, eq);
+          t.template unit<true, false>(i, eq);
 #pragma unroll
           for (int k = 0; k < G::PV; ++k) {
             sq[k] = wt.Q(eq[k]);
@@ -277,10 +289,11 @@ __device__ inline void stream_row(const void* rp, const void* rq, const FastWeig
               sm[k] += sm[k + h];
             }
           }
-        up[i] = sp[0];
+        const bool in = t.is_live(i);  // a repeated last unit adds nothing
+        up[i] = in ? sp[0] : 0.f;
         if constexpr (!BONUS) {
-          uq[i] = sq[0];
-          um[i] = sm[0];
+          uq[i] = in ? sq[0] : 0.f;
+          um[i] = in ? sm[0] : 0.f;
         } else {
           uq[i] = um[i] = 0.f;
         }
@@ -343,12 +356,12 @@ __device__ inline bool rescan_segment(const void* rp, const void* rq, const Fast
       float wv[G::PV];
       {
         float ep[G::PV];
-        tl.template unit<false>(i, ep);
+        tl.template unit<false, true>(i, ep);
 #pragma unroll
         for (int k = 0; k < G::PV; ++k) wv[k] = wt.P(ep[k]);
         if constexpr (!BONUS) {
           float eq[G::PV];
-          tl.template unit<true>(i, eq);
+          tl.template unit<true, true>(i, eq);
 #pragma unroll
           for (int k = 0; k < G::PV; ++k) wv[k] = fmaxf(wv[k] - wt.Q(eq[k]), 0.f);
         }

@@ -10,7 +10,7 @@ namespace sv {
 constexpr int kBlock = 256;   // threads per workgroup in every kernel
 constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kWaves = kBlock / kWave;
-constexpr int kMaxDrawChunks = 64;    // fp64 draw chunks per row: one wave combines them
+constexpr int kMaxDrawChunks = 256;   // fp64 draw chunks per row: one wave combines them, 4 per lane
 
 // Elements one lane of the row sweep holds: six 16-byte units on the vector
 // path, sixteen single elements on the scalar path.
