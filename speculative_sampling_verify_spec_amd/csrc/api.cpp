@@ -150,6 +150,7 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   const double c64 = M_LOG2E / T64;
   P.c = static_cast<float>(c64);
   P.inv_t = 1.0 / T64;
+  P.ec = make_exp_consts();
   P.rec = reinterpret_cast<SeqRec*>(ws + L.rec);
   P.xsum = reinterpret_cast<double*>(ws + L.xsum);
   P.queue = reinterpret_cast<int32_t*>(ws + L.queue);

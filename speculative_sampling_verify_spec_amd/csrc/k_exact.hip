@@ -36,17 +36,20 @@ constexpr int kRun = 8;                          // elements per lane per rescan
 constexpr int kRound = kXBlock * kRun;           // 1024 elements per round (the smallest chunk)
 constexpr double kKappa = 1e-4;                  // near-flip window, relative to Q
 constexpr unsigned kExactSeqs = 32;              // queued sequences the kernels cover per pass
+constexpr int kMaxPer = (kMaxDrawChunks + kWave - 1) / kWave;  // chunks per lane in the select
 
 // fp64 weight exp(x / T - L'), L' the natural-log reference.
 struct ExactWeight {
   double inv_t, ap, aq;
-  __device__ double P(float x) const { return exp_f64(static_cast<double>(x) * inv_t - ap); }
-  __device__ double Q(float x) const { return exp_f64(static_cast<double>(x) * inv_t - aq); }
+  ExpConsts ec;
+  __device__ double P(float x) const { return exp_f64(static_cast<double>(x) * inv_t - ap, ec); }
+  __device__ double Q(float x) const { return exp_f64(static_cast<double>(x) * inv_t - aq, ec); }
 };
 
 __device__ inline ExactWeight exact_weight(const Params& p, const SeqRec& rec) {
   ExactWeight e;
   e.inv_t = p.inv_t;
+  e.ec = p.ec;
   e.ap = rec.lzp * M_LN2;
   e.aq = rec.lzq * M_LN2;
   return e;
@@ -188,14 +191,21 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
   __shared__ double s_base;
   __shared__ int s_chunk, s_usep, s_exact_total;
   if (threadIdx.x < kWave) {
-    // lane l owns chunks l*per .. l*per + per - 1
+    // lane l owns chunks l*per .. l*per + per - 1 (per <= kMaxPer); their
+    // sums are loaded together up front
     const int per = (p.R3 + kWave - 1) / kWave;
-    auto cs = [&](int k, int f) {
+    double cv[kMaxPer][5];
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
       const int c = lane * per + k;
-      return c < p.R3 ? cs_base[c * 5 + f] : 0.0;
-    };
+      const bool in = k < per && c < p.R3;
+#pragma unroll
+      for (int f = 0; f < 5; ++f) cv[k][f] = in ? cs_base[c * 5 + f] : 0.0;
+    }
+    auto cs = [&](int k, int f) { return cv[k][f]; };
     double sp_l = 0.0, sq_l = 0.0;
-    for (int k = 0; k < per; ++k) {
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
       sp_l += cs(k, 0);
       if (!bonus) sq_l += cs(k, 1);
     }
@@ -212,12 +222,14 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
       const double SQ = wave_sum(sq_l);
       rho = SP / SQ;
       double z_l = 0.0;
-      for (int k = 0; k < per; ++k) z_l += mass(k, false);
+#pragma unroll
+      for (int k = 0; k < kMaxPer; ++k) z_l += mass(k, false);
       usep = !(wave_sum(z_l) > 0.0);  // p == q to rounding: draw from p_n instead
     }
     const bool use_p = bonus || usep;
     double v = 0.0, err = 0.0;
-    for (int k = 0; k < per; ++k) {
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
       v += mass(k, use_p);
       err += merr(k, use_p);
     }
@@ -239,21 +251,23 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
       int last = lane * per;
       double run_last = run, erun_last = erun;
       rc = -1;
-      for (int k = 0; k < per; ++k) {
+#pragma unroll
+      for (int k = 0; k < kMaxPer; ++k) {  // chunks past the row have no mass
         const int c = lane * per + k;
-        if (c >= p.R3) break;
         const double m = mass(k, use_p);
-        if (hit && run + m > t) {
-          rc = c;
-          break;
+        if (rc < 0 && k < per && c < p.R3) {
+          if (hit && run + m > t) {
+            rc = c;
+          } else {
+            if (m > 0.0) {
+              last = c;
+              run_last = run;
+              erun_last = erun;
+            }
+            run += m;
+            erun += merr(k, use_p);
+          }
         }
-        if (m > 0.0) {
-          last = c;
-          run_last = run;
-          erun_last = erun;
-        }
-        run += m;
-        erun += merr(k, use_p);
       }
       if (rc < 0) {
         rc = last;

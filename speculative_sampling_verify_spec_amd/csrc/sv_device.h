@@ -68,29 +68,22 @@ __device__ inline float load_masked(const void* row, long i, long end) {
 // callers only feed it values <= 0 whose tiny results do not matter.
 __device__ inline float ex2(float t) { return __builtin_amdgcn_exp2f(t); }
 
-// exp(y) in fp64 for the refine path (about 19 instructions against roughly
-// a hundred for the general library routine).  Cody-Waite reduction
+// exp(y) in fp64 for the exact draw (about 20 instructions against roughly a
+// hundred for the general library routine).  Cody-Waite reduction
 // y = k ln2 + r with ln2 split into a high part whose low 21 mantissa bits are
 // zero (so k * hi is exact) and the rounded remainder; then the degree-12
 // Taylor polynomial of e^r on |r| <= ln2/2 (truncation below 1.7e-16
 // relative) by Horner's rule, and an exact scale by 2^k.  Arguments below
-// -745.5 (where e^y underflows to zero) and NaN return 0.
-__host__ __device__ inline double exp_f64(double y) {
+// -745.5 (where e^y underflows to zero) and NaN return 0.  The constants come
+// in `e` (kernel arguments, hence scalar registers).
+__device__ inline double exp_f64(double y, const ExpConsts& e) {
   if (!(y > -745.5)) return 0.0;
-  const double k = rint(y * 1.4426950408889634);
-  double r = fma(-k, 0x1.62e42fee00000p-1, y);
-  r = fma(-k, 0x1.a39ef35793c76p-33, r);
-  double q = 2.08767569878681e-09;   // 1/12!
-  q = fma(q, r, 2.505210838544172e-08);
-  q = fma(q, r, 2.755731922398589e-07);
-  q = fma(q, r, 2.7557319223985893e-06);
-  q = fma(q, r, 2.48015873015873e-05);
-  q = fma(q, r, 0.0001984126984126984);
-  q = fma(q, r, 0.001388888888888889);
-  q = fma(q, r, 0.008333333333333333);
-  q = fma(q, r, 0.041666666666666664);
-  q = fma(q, r, 0.16666666666666666);
-  q = fma(q, r, 0.5);
+  const double k = rint(y * e.log2e);
+  double r = fma(-k, e.ln2_hi, y);
+  r = fma(-k, e.ln2_lo, r);
+  double q = e.inv_fact[0];
+#pragma unroll
+  for (int i = 1; i < 11; ++i) q = fma(q, r, e.inv_fact[i]);
   q = fma(q, r, 1.0);
   q = fma(q, r, 1.0);
   return ldexp(q, static_cast<int>(k));

@@ -27,6 +27,29 @@ struct SeqRec {
 };
 static_assert(sizeof(SeqRec) == 24, "SeqRec layout");
 
+// Constants of the fp64 exp: the Cody-Waite split of ln 2 and the Taylor
+// coefficients 1/n!.  They travel as kernel arguments, so the kernels read
+// them from scalar registers instead of rebuilding 64-bit literals per use.
+struct ExpConsts {
+  double log2e;
+  double ln2_hi;        // ln 2 with its low 21 mantissa bits zero: k * ln2_hi is exact for |k| < 2^21
+  double ln2_lo;        // ln 2 - ln2_hi, rounded
+  double inv_fact[11];  // 1/12!, 1/11!, ..., 1/2!
+};
+
+inline ExpConsts make_exp_consts() {
+  ExpConsts e{};
+  e.log2e = 1.4426950408889634;
+  e.ln2_hi = 0x1.62e42fee00000p-1;
+  e.ln2_lo = 0x1.a39ef35793c76p-33;
+  double f = 1.0;
+  for (int n = 2; n <= 12; ++n) {
+    f *= n;
+    e.inv_fact[12 - n] = 1.0 / f;  // exact factorials; one rounding each
+  }
+  return e;
+}
+
 // Everything a kernel needs, passed by value.
 struct Params {
   const void* lp;            // [B][K+1][V] target logits
@@ -38,6 +61,7 @@ struct Params {
   int vec;                   // 1: 16-byte vector loads are legal for every row
   float c;                   // log2(e) / T rounded to fp32
   double inv_t;              // 1 / T in fp64 (exact draw)
+  ExpConsts ec;              // fp64 exp constants (exact draw)
   int32_t* out_tokens;       // [B][K+1]
   int32_t* out_n;            // [B]
   float* out_logz;           // [B][2K+1] or null
