@@ -231,3 +231,45 @@ def test_excused_budget_over_many_seeds(gpu_lib):
         exc += rep.excused
     say(f"[parity] many seeds: decisions={dec} excused={exc}")
     assert exc <= 1e-4 * dec
+
+
+def test_fp64_queue_longer_than_one_pass(gpu_lib):
+    """512 sequences of the small bf16 recipe: about a fifth of their draws
+    are not certified by the fast path (its distributions are flat), far more
+    than the 32 sequences the fp64 kernels take per pass, so their grids loop."""
+    wl = dataclasses.replace(workloads.WORKLOADS[1], B=512)
+    b = workloads.make_batch(1, wl=wl, seed=77, workers=workloads.default_workers())
+    say(f"[parity] long fp64 queue {wl.describe()}")
+    g = run_gpu(gpu_lib, b)
+    ref = oracle.verify_batch(b)
+    compare(b, g, ref).check()
+    same = np.flatnonzero(g.n == ref.n_accepted)
+    np.testing.assert_array_equal(g.tokens[same], ref.tokens[same])
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 2_200_000, "bf16", 1.0), (2, 1, 600_001, "fp32", 0.9)],
+                         ids=lambda s: "B{}K{}V{}{}T{}".format(*s))
+def test_rows_longer_than_the_segment_table(gpu_lib, shape):
+    """Rows so long that a draw segment spans several wave iterations (the
+    segment table holds 1024 entries), on the vector and on the scalar path."""
+    B, K, V, dt, T = shape
+    wl = workloads.Workload("long", B, K, V, dt, float(np.float32(T)), 2.0, 1.1, "noise", 0.8)
+    b = workloads.make_batch(1, wl=wl, seed=9)
+    say(f"[parity] long rows {wl.describe()}")
+    compare(b, run_gpu(gpu_lib, b), oracle.verify_batch(b)).check()
+
+
+def test_resample_uniform_at_the_ends_of_its_grid(gpu_lib):
+    """The smallest and the largest uniform of the grid: the draw's first
+    token with weight, and the end of the row where rounding can leave the
+    running sum short of u * Z."""
+    b = workloads.make_batch(1, seed=5, workers=workloads.default_workers())
+    ur = b.u_resample.copy()
+    ur[: b.B // 2] = np.float32(0.5 * 2.0 ** -23)
+    ur[b.B // 2:] = np.float32(1.0 - 0.5 * 2.0 ** -23)
+    b2 = dataclasses.replace(b, u_resample=ur)
+    g = run_gpu(gpu_lib, b2)
+    ref = oracle.verify_batch(b2)
+    compare(b2, g, ref).check()
+    same = np.flatnonzero(g.n == ref.n_accepted)
+    np.testing.assert_array_equal(g.tokens[same], ref.tokens[same])
