@@ -52,13 +52,16 @@ def compare(batch, gpu: GpuOut, ref: oracle.Result, rows: np.ndarray | None = No
     oracle's results for the same sequences, in the same order."""
     rows = np.arange(batch.B) if rows is None else np.asarray(rows)
     K = batch.K
+    nd = getattr(batch, "num_drafts", None)
+    kbs = np.full(batch.B, K) if nd is None else np.asarray(nd)
     failures, excused = [], 0
     greedy = batch.T == 0.0
     max_lz = 0.0
     for i, b in enumerate(rows):
         gt, gn = gpu.tokens[b], int(gpu.n[b])
         ot, on = ref.tokens[i], int(ref.n_accepted[i])
-        if not (0 <= gn <= K) or np.any(gt[gn + 1:] != -1) or list(gt[:gn]) != list(batch.draft_tokens[b, :gn]):
+        kb = int(kbs[b])
+        if not (0 <= gn <= kb) or np.any(gt[gn + 1:] != -1) or list(gt[:gn]) != list(batch.draft_tokens[b, :gn]):
             failures.append((int(b), "malformed output", gt.tolist(), gn))
             continue
         if gpu.flags[b] & 4 != ref.flags[i] & 4 and gn == on:
@@ -67,8 +70,10 @@ def compare(batch, gpu: GpuOut, ref: oracle.Result, rows: np.ndarray | None = No
             if gn != on or not np.array_equal(gt, ot):
                 failures.append((int(b), "greedy", gt.tolist(), ot.tolist()))
             continue
-        lz = gpu.logz[b].astype(np.float64)
-        max_lz = max(max_lz, float(np.max(np.abs(lz - ref.logz[i]) / np.maximum(1.0, np.abs(ref.logz[i])))))
+        used = np.isfinite(ref.logz[i])  # rows the sequence uses (all of them unless K_b < K)
+        lz = gpu.logz[b].astype(np.float64)[used]
+        rz = ref.logz[i][used]
+        max_lz = max(max_lz, float(np.max(np.abs(lz - rz) / np.maximum(1.0, np.abs(rz)))))
         if gn != on:
             k = min(gn, on)
             margin = abs(float(batch.u_accept[b, k]) - ref.thr[i, k])
@@ -82,7 +87,8 @@ def compare(batch, gpu: GpuOut, ref: oracle.Result, rows: np.ndarray | None = No
             if not (0 <= j < batch.V):
                 failures.append((int(b), "draw out of range", j))
                 continue
-            lo, hi = oracle.draw_interval(batch.logits_p[b], None if batch.logits_q is None else batch.logits_q[b],
+            lo, hi = oracle.draw_interval(batch.logits_p[b][: kb + 1],
+                                          None if batch.logits_q is None else batch.logits_q[b][:kb],
                                           gn, j, float(batch.u_resample[b]), batch.T, batch.dtype)
             u = float(batch.u_resample[b])
             dist = 0.0 if lo <= u < hi else min(abs(u - lo), abs(u - hi))
@@ -90,5 +96,5 @@ def compare(batch, gpu: GpuOut, ref: oracle.Result, rows: np.ndarray | None = No
                 excused += 1
             else:
                 failures.append((int(b), "draw", j, int(ot[on]), dist))
-    decisions = int(np.sum(np.minimum(ref.n_accepted + 1, K)) + len(rows))
+    decisions = int(np.sum(np.minimum(ref.n_accepted + 1, kbs[rows])) + len(rows))
     return Report(len(rows), decisions, excused, failures, max_lz)

@@ -193,11 +193,18 @@ def verify_greedy_sequence(lp: np.ndarray, x: np.ndarray):
 
 
 def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, dtype: str,
-           seqs: Optional[np.ndarray] = None) -> Result:
+           seqs: Optional[np.ndarray] = None, num_drafts: Optional[np.ndarray] = None) -> Result:
     """Verify every sequence (or the subset ``seqs``) of a batch.
 
     logits_p [B,K+1,V], logits_q [B,K,V] (ignored when T == 0), draft_tokens
-    [B,K], u_accept [B,K], u_resample [B]; logits as float32 or bf16 bits."""
+    [B,K], u_accept [B,K], u_resample [B]; logits as float32 or bf16 bits.
+
+    ``num_drafts`` [B] (optional) gives sequence b its own draft count
+    0 <= K_b <= K, as when the draft length is adapted per sequence ([B]
+    "最优猜测长度 k：贪心还是保守？"): only its first K_b + 1 target rows, first
+    K_b draft rows, drafts and accept uniforms take part, the bonus row is
+    p_{K_b}, and outputs past the emitted token are -1 up to K + 1 entries.
+    Rows a sequence does not use have NaN log normalisers."""
     B, K1, V = np.shape(logits_p)
     K = K1 - 1
     idx = np.arange(B) if seqs is None else np.asarray(seqs)
@@ -208,28 +215,45 @@ def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, dty
                  bonus=np.zeros(S, bool), flags=np.zeros(S, np.int32))
     T = float(np.float32(T))
     for i, b in enumerate(idx):
-        x = np.asarray(draft_tokens[b])
+        kb = K if num_drafts is None else int(num_drafts[b])
+        x = np.asarray(draft_tokens[b])[:kb]
         if T == 0.0:
-            r = verify_greedy_sequence(widen(logits_p[b], dtype), x)
+            r = verify_greedy_sequence(widen(logits_p[b][: kb + 1], dtype), x)
         else:
-            yp = widen(logits_p[b], dtype) / T
-            yq = widen(logits_q[b], dtype) / T
-            r = verify_sequence(yp, yq, x, np.asarray(u_accept[b]), float(u_resample[b]))
-            out.logz[i] = r["logz"]
-            out.thr[i] = r["thr"]
+            yp = widen(logits_p[b][: kb + 1], dtype) / T
+            yq = widen(logits_q[b][:kb], dtype) / T
+            r = verify_sequence(yp, yq, x, np.asarray(u_accept[b])[:kb], float(u_resample[b]))
+            out.logz[i, : kb + 1] = r["logz"][: kb + 1]
+            out.logz[i, K + 1: K + 1 + kb] = r["logz"][kb + 1:]
+            out.thr[i, :kb] = r["thr"]
             out.draw_lo[i] = r["lo"]
             out.draw_hi[i] = r["hi"]
             out.bonus[i] = r["bonus"]
-        out.tokens[i] = r["tokens"]
+        out.tokens[i, : kb + 1] = r["tokens"]
         out.n_accepted[i] = r["n"]
         out.flags[i] = r["flags"]
     return out
 
 
+def position_stats(n_accepted: np.ndarray, num_drafts: np.ndarray, K: int) -> np.ndarray:
+    """Per-position acceptance counters ([D] "Когда процент принятия падает":
+    acceptance changes with the position in the draft; [D] "Мониторинг в
+    производстве": it is the quantity to watch).  Returns [2K] integers:
+    evaluated[k], then accepted[k].  Position k of a sequence is evaluated
+    when all earlier drafts were accepted (k <= n) and it exists (k < K_b); it
+    is accepted when k < n."""
+    n = np.asarray(n_accepted)[:, None]
+    kb = np.asarray(num_drafts)[:, None]
+    k = np.arange(K)[None, :]
+    evaluated = np.sum((k <= n) & (k < kb), axis=0)
+    accepted = np.sum(k < n, axis=0)
+    return np.concatenate([evaluated, accepted]).astype(np.int64)
+
+
 def verify_batch(batch, seqs: Optional[np.ndarray] = None) -> Result:
     """Convenience wrapper for a ``workloads.Batch``-like object."""
     return verify(batch.logits_p, batch.logits_q, batch.draft_tokens, batch.u_accept,
-                  batch.u_resample, batch.T, batch.dtype, seqs)
+                  batch.u_resample, batch.T, batch.dtype, seqs, getattr(batch, "num_drafts", None))
 
 
 def draw_interval(logits_p_seq, logits_q_seq, n: int, j: int, u: float, T: float, dtype: str):

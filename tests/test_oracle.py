@@ -369,3 +369,81 @@ def test_batch_api_on_a_generated_workload():
         assert 0 <= r.tokens[i, n] < b.V and np.all(r.tokens[i, n + 1:] == -1)
         assert r.draw_lo[i] <= b.u_resample[i] < r.draw_hi[i]
     assert r.decisions() == int(np.sum(np.minimum(r.n_accepted + 1, b.K)) + 6)
+
+
+# ------------------------------------------------------- ragged draft counts --
+def test_ragged_mean_emitted_follows_truncated_geometric():
+    """Each sequence with its own draft count K_b ([B] "最优猜测长度 k"): with
+    per-position acceptance a = sum(min(p, q)) = 0.8 the mean number of tokens
+    per round of the sequences with K_b = k is (1 - a^(k+1)) / (1 - a) ([B]
+    "加速比公式"), including k = 0 (one token, never a draft)."""
+    rng = np.random.default_rng(5)
+    K, V, N, a = 5, 2, 24000, 0.8
+    q0 = 1.5 - a
+    lp = np.zeros((N, K + 1, V), np.float32)
+    lq = np.tile(np.log(np.array([q0, 1 - q0], np.float32)), (N, K, 1)).astype(np.float32)
+    x = (rng.random((N, K)) >= q0).astype(np.int32)
+    kb = rng.integers(0, K + 1, N)
+    r = oracle.verify(lp, lq, x, rng.random((N, K), np.float32), rng.random(N, np.float32), 1.0, "fp32",
+                      num_drafts=kb)
+    assert np.all(r.n_accepted <= kb)
+    for k in range(K + 1):
+        sel = kb == k
+        mean = float(np.mean(r.n_accepted[sel] + 1))
+        closed = (1 - a ** (k + 1)) / (1 - a)
+        assert abs(mean - closed) < 5 * 1.8 / np.sqrt(sel.sum()), (k, mean, closed)
+    # nothing past a sequence's own drafts is emitted or tested
+    for i in range(200):
+        assert np.all(r.tokens[i, r.n_accepted[i] + 1:] == -1)
+        assert np.all(np.isnan(r.thr[i, kb[i]:]))
+
+
+def test_zero_drafts_draw_from_p0_by_searchsorted():
+    """K_b = 0: no test, the token is p_0's inverse CDF (numpy's searchsorted
+    on the cumulative sum, side="right")."""
+    rng = np.random.default_rng(6)
+    B, K, V = 64, 3, 50
+    lp = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    lq = rng.normal(0, 2, (B, K, V)).astype(np.float32)
+    ur = rng.random(B, np.float32)
+    r = oracle.verify(lp, lq, rng.integers(0, V, (B, K)).astype(np.int32), rng.random((B, K), np.float32), ur,
+                      0.9, "fp32", num_drafts=np.zeros(B, np.int64))
+    T = float(np.float32(0.9))
+    for b in range(B):
+        p = softmax(lp[b, 0].astype(np.float64) / T)
+        c = np.cumsum(p)
+        assert r.n_accepted[b] == 0
+        assert r.tokens[b, 0] == min(int(np.searchsorted(c, float(ur[b]) * c[-1], side="right")), V - 1)
+        assert np.all(r.tokens[b, 1:] == -1)
+
+
+def test_position_stats_worked_example():
+    """Three sequences, counted by hand.  (K_b, n): (3, 1) evaluates positions
+    0, 1 and accepts 0; (2, 2) evaluates 0, 1 and accepts both; (0, 0)
+    evaluates nothing."""
+    s = oracle.position_stats(np.array([1, 2, 0]), np.array([3, 2, 0]), K=3)
+    np.testing.assert_array_equal(s, [2, 2, 0, 2, 1, 0])
+
+
+def test_position_acceptance_rates_follow_sum_of_min():
+    """Per-position acceptance frequency accepted[k] / evaluated[k] against
+    sum(min(p_k, q_k)) ([B] "验收标准的精确数学"), with a different rate at
+    every position, ragged K_b; and evaluated[k+1] = accepted[k] minus the
+    sequences that accepted all K_b = k+1 drafts."""
+    rng = np.random.default_rng(8)
+    K, V, N = 4, 2, 20000
+    q0s = np.array([0.55, 0.75, 0.9, 0.65])      # rates 0.95, 0.75, 0.6, 0.85
+    lp = np.zeros((N, K + 1, V), np.float32)
+    lq = np.stack([np.tile(np.log(np.array([q, 1 - q], np.float32)), (N, 1)) for q in q0s], axis=1)
+    x = (rng.random((N, K)) >= q0s[None, :]).astype(np.int32)
+    kb = rng.integers(1, K + 1, N)
+    r = oracle.verify(lp, lq.astype(np.float32), x, rng.random((N, K), np.float32), rng.random(N, np.float32),
+                      1.0, "fp32", num_drafts=kb)
+    s = oracle.position_stats(r.n_accepted, kb, K)
+    ev, ac = s[:K], s[K:]
+    for k in range(K):
+        beta = 1.5 - q0s[k]
+        assert abs(ac[k] / ev[k] - beta) < 5 * np.sqrt(beta * (1 - beta) / ev[k]), (k, ac[k] / ev[k], beta)
+    for k in range(K - 1):
+        full = np.sum((kb == k + 1) & (r.n_accepted == k + 1))
+        assert ev[k + 1] == ac[k] - full

@@ -190,6 +190,7 @@ class Batch:
     draft_tokens: np.ndarray         # [B,K] int32
     u_accept: np.ndarray             # [B,K] float32
     u_resample: np.ndarray           # [B] float32
+    num_drafts: Optional[np.ndarray] = None  # [B] int32 per-sequence draft counts K_b, or None (all K)
 
     @property
     def B(self) -> int:
@@ -259,6 +260,13 @@ def custom_batch(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: floa
                  draft_tokens=np.asarray(draft_tokens, dtype=np.int32).reshape(B, K1 - 1),
                  u_accept=None if u_accept is None else np.asarray(u_accept, dtype=np.float32).reshape(B, K1 - 1),
                  u_resample=None if u_resample is None else np.asarray(u_resample, dtype=np.float32).reshape(B))
+
+
+def ragged_draft_counts(B: int, K: int, seed: int = DEFAULT_SEED, low: int = 1) -> np.ndarray:
+    """Per-sequence draft counts K_b, uniform on [low, K], seeded: the
+    stand-in for a proposer that adapts its draft length per sequence."""
+    rng = np.random.default_rng(np.random.SeedSequence(entropy=[seed, 9001]))
+    return rng.integers(low, K + 1, B).astype(np.int32)
 
 
 def to_device(batch: Batch, device="cuda"):
