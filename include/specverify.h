@@ -124,6 +124,37 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
                    void* workspace, size_t workspace_bytes, void* stream,
                    float* out_logz, int32_t* out_flags, void* ev_sweep_begin, void* ev_sweep_end);
 
+/*
+ * spec_verify_ragged - spec_verify with a draft count per sequence, and
+ * optional per-position acceptance counters.
+ *
+ * num_drafts     [B] int32 (device): sequence b uses its first K_b drafts,
+ *                0 <= K_b <= K (values outside are clamped), as when the
+ *                draft length is adapted per sequence ([B] "最优猜测长度 k：
+ *                贪心还是保守？", adaptive k).  Layouts stay those of
+ *                spec_verify, padded to K: target rows past K_b, draft rows,
+ *                drafts and accept uniforms past K_b - 1 are not read.  A
+ *                sequence that accepts all K_b drafts takes its bonus token
+ *                from target row K_b.  out_tokens keeps K+1 entries per
+ *                sequence, -1 after the emitted token.  In sampling mode the
+ *                sequence's rows of out_logz that it does not use are not
+ *                written.
+ * position_stats [2K] uint64 (device) or NULL: counters this call adds to
+ *                (the caller zeroes them once): position_stats[k] counts the
+ *                sequences whose draft k was tested (k <= n and k < K_b),
+ *                position_stats[K + k] those whose draft k was accepted
+ *                (k < n).  Acceptance by draft position is what [D] "Когда
+ *                процент принятия падает" and "Мониторинг в производстве"
+ *                watch.  Calls adding to the same counters must not overlap.
+ * All other arguments, the workspace size and the return codes are those of
+ * spec_verify; num_drafts may not be NULL.
+ */
+int spec_verify_ragged(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
+                       const int32_t* num_drafts, const float* u_accept, const float* u_resample, float T,
+                       int B, int K, int V, int32_t* out_tokens, int32_t* out_n_accepted,
+                       uint64_t* position_stats, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* Static description of a return code. */
 const char* spec_verify_strerror(int code);
 

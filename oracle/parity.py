@@ -28,8 +28,8 @@ LOGZ_TOL = 1e-5
 class GpuOut:
     tokens: np.ndarray
     n: np.ndarray
-    logz: np.ndarray | None
-    flags: np.ndarray
+    logz: np.ndarray | None     # None: not returned (then not compared)
+    flags: np.ndarray | None
 
 
 @dataclasses.dataclass
@@ -64,16 +64,17 @@ def compare(batch, gpu: GpuOut, ref: oracle.Result, rows: np.ndarray | None = No
         if not (0 <= gn <= kb) or np.any(gt[gn + 1:] != -1) or list(gt[:gn]) != list(batch.draft_tokens[b, :gn]):
             failures.append((int(b), "malformed output", gt.tolist(), gn))
             continue
-        if gpu.flags[b] & 4 != ref.flags[i] & 4 and gn == on:
+        if gpu.flags is not None and gpu.flags[b] & 4 != ref.flags[i] & 4 and gn == on:
             failures.append((int(b), "bad-draft flag", int(gpu.flags[b]), int(ref.flags[i])))
         if greedy:
             if gn != on or not np.array_equal(gt, ot):
                 failures.append((int(b), "greedy", gt.tolist(), ot.tolist()))
             continue
-        used = np.isfinite(ref.logz[i])  # rows the sequence uses (all of them unless K_b < K)
-        lz = gpu.logz[b].astype(np.float64)[used]
-        rz = ref.logz[i][used]
-        max_lz = max(max_lz, float(np.max(np.abs(lz - rz) / np.maximum(1.0, np.abs(rz)))))
+        if gpu.logz is not None:
+            used = np.isfinite(ref.logz[i])  # rows the sequence uses (all of them unless K_b < K)
+            lz = gpu.logz[b].astype(np.float64)[used]
+            rz = ref.logz[i][used]
+            max_lz = max(max_lz, float(np.max(np.abs(lz - rz) / np.maximum(1.0, np.abs(rz)))))
         if gn != on:
             k = min(gn, on)
             margin = abs(float(batch.u_accept[b, k]) - ref.thr[i, k])

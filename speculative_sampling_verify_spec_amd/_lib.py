@@ -22,8 +22,8 @@ ERRORS = {0: "SPECV_OK", -1: "SPECV_E_NULL", -2: "SPECV_E_SHAPE", -3: "SPECV_E_D
           -5: "SPECV_E_WORKSPACE", -6: "SPECV_E_ALIGN", -7: "SPECV_E_HIP"}
 
 # every symbol include/specverify.h declares
-EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_ex", "spec_verify_strerror",
-           "spec_verify_version")
+EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_ex", "spec_verify_ragged",
+           "spec_verify_strerror", "spec_verify_version")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -54,6 +54,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify.restype = i32
     lib.spec_verify_ex.argtypes = common + [vp, vp, vp, vp]
     lib.spec_verify_ex.restype = i32
+    lib.spec_verify_ragged.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
+    lib.spec_verify_ragged.restype = i32
     lib.spec_verify_strerror.argtypes = [i32]
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     lib.spec_verify_version.argtypes = []
@@ -107,8 +109,24 @@ def spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float
     return int(lib.spec_verify_ex(*args, _ptr(out_logz), _ptr(out_flags), e0, e1))
 
 
+def spec_verify_ragged(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T: float,
+                       out_tokens=None, out_n_accepted=None, workspace=None, *, position_stats=None,
+                       stream=None) -> int:
+    """Raw call of spec_verify_ragged; returns the library's status code."""
+    lib = load()
+    B, K1, V = logits_p.shape
+    import torch
+    st = stream if stream is not None else torch.cuda.current_stream(logits_p.device).cuda_stream
+    return int(lib.spec_verify_ragged(_ptr(logits_p), _ptr(logits_q), _ptr(draft_tokens), _ptr(num_drafts),
+                                      _ptr(u_accept), _ptr(u_resample), float(T), B, K1 - 1, V, _ptr(out_tokens),
+                                      _ptr(out_n_accepted), _ptr(position_stats), _dtype_code(logits_p),
+                                      _ptr(workspace),
+                                      0 if workspace is None else workspace.numel() * workspace.element_size(), st))
+
+
 def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
-           return_logz: bool = False, return_flags: bool = False, workspace=None, events=None):
+           return_logz: bool = False, return_flags: bool = False, workspace=None, events=None,
+           num_drafts=None, position_stats=None):
     """One verify step on torch device tensors.
 
     logits_p [B,K+1,V] and logits_q [B,K,V] (bf16 or fp32, contiguous, same
@@ -116,7 +134,12 @@ def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
     float32; logits_q / u_accept / u_resample may be None when T == 0.
     Returns (tokens [B,K+1] int32, n_accepted [B] int32) plus log Z
     [B,2K+1] float32 and flags [B] int32 when asked.  Runs on torch's current
-    stream; nothing synchronises."""
+    stream; nothing synchronises.
+
+    num_drafts [B] int32 (device) gives every sequence its own draft count
+    (spec_verify_ragged); position_stats [2K] int64 (device, zeroed by the
+    caller) then receives the per-position tested / accepted counts.  Neither
+    combines with return_logz, return_flags or events."""
     import torch
     dev = logits_p.device
     if dev.type != "cuda":
@@ -141,6 +164,17 @@ def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
             raise ValueError("u_resample must be float32 [B]")
     else:
         logits_q = u_accept = u_resample = None
+    if num_drafts is not None:
+        if num_drafts.device != dev or num_drafts.dtype != torch.int32 or tuple(num_drafts.shape) != (B,):
+            raise ValueError("num_drafts must be an int32 [B] tensor on the logits' device")
+        if return_logz or return_flags or events is not None:
+            raise ValueError("num_drafts does not combine with return_logz, return_flags or events")
+    if position_stats is not None:
+        if num_drafts is None:
+            raise ValueError("position_stats needs num_drafts")
+        if position_stats.device != dev or position_stats.dtype != torch.int64 or \
+                tuple(position_stats.shape) != (2 * K,) or not position_stats.is_contiguous():
+            raise ValueError("position_stats must be a contiguous int64 [2K] tensor on the logits' device")
     dt = _dtype_code(logits_p)
     need = workspace_size(B, K, V, dt, float(T))
     if need == 0:
@@ -151,8 +185,12 @@ def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
     n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
     logz = torch.empty((B, 2 * K + 1), dtype=torch.float32, device=dev) if return_logz else None
     flags = torch.empty((B,), dtype=torch.int32, device=dev) if return_flags else None
-    rc = spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T, tokens, n_acc, workspace,
-                     out_logz=logz, out_flags=flags, events=events)
+    if num_drafts is not None:
+        rc = spec_verify_ragged(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T, tokens,
+                                n_acc, workspace, position_stats=position_stats)
+    else:
+        rc = spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T, tokens, n_acc, workspace,
+                         out_logz=logz, out_flags=flags, events=events)
     if rc != 0:
         raise SpecVerifyError(rc, strerror(rc))
     out = (tokens, n_acc)

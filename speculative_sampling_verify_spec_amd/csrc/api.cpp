@@ -92,12 +92,15 @@ size_t spec_verify_workspace_size(int B, int K, int V, int dtype, float T) {
   return a > b ? a : b;
 }
 
-int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
-                   const float* u_accept, const float* u_resample, float T, int B, int K, int V,
-                   int32_t* out_tokens, int32_t* out_n_accepted, int dtype,
-                   void* workspace, size_t workspace_bytes, void* stream,
-                   float* out_logz, int32_t* out_flags, void* ev_sweep_begin, void* ev_sweep_end) {
-  using namespace sv;
+namespace sv {
+namespace {
+
+// Every entry point: host-side checks, then the launches on `stream`.
+int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft_tokens, const int32_t* num_drafts,
+                const float* u_accept, const float* u_resample, float T, int B, int K, int V,
+                int32_t* out_tokens, int32_t* out_n_accepted, unsigned long long* position_stats, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream, float* out_logz, int32_t* out_flags,
+                void* ev_sweep_begin, void* ev_sweep_end) {
   if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_E_DTYPE;
   if (!valid_temperature(T)) return SPECV_E_TEMP;
   const bool greedy = T == 0.f;
@@ -120,6 +123,8 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   P.x = draft_tokens;
   P.ua = u_accept;
   P.ur = u_resample;
+  P.kb = num_drafts;
+  P.stats = position_stats;
   P.B = B;
   P.K = K;
   P.V = V;
@@ -143,6 +148,7 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
     if (launch_sweep_argmax(P, dtype, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
       return SPECV_E_HIP;
     if (launch_greedy_scan(P, st) != hipSuccess) return SPECV_E_HIP;
+    if (position_stats && launch_position_stats(P, st) != hipSuccess) return SPECV_E_HIP;
     return SPECV_OK;
   }
 
@@ -161,7 +167,32 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   if (launch_sweep_lse(P, dtype, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess) return SPECV_E_HIP;
   if (launch_verify(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   if (launch_exact(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
+  if (position_stats && launch_position_stats(P, st) != hipSuccess) return SPECV_E_HIP;
   return SPECV_OK;
+}
+
+}  // namespace
+}  // namespace sv
+
+int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
+                   const float* u_accept, const float* u_resample, float T, int B, int K, int V,
+                   int32_t* out_tokens, int32_t* out_n_accepted, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream,
+                   float* out_logz, int32_t* out_flags, void* ev_sweep_begin, void* ev_sweep_end) {
+  return sv::verify_impl(logits_p, logits_q, draft_tokens, nullptr, u_accept, u_resample, T, B, K, V, out_tokens,
+                         out_n_accepted, nullptr, dtype, workspace, workspace_bytes, stream, out_logz, out_flags,
+                         ev_sweep_begin, ev_sweep_end);
+}
+
+int spec_verify_ragged(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
+                       const int32_t* num_drafts, const float* u_accept, const float* u_resample, float T,
+                       int B, int K, int V, int32_t* out_tokens, int32_t* out_n_accepted,
+                       uint64_t* position_stats, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!num_drafts) return SPECV_E_NULL;
+  return sv::verify_impl(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T, B, K, V, out_tokens,
+                         out_n_accepted, reinterpret_cast<unsigned long long*>(position_stats), dtype, workspace,
+                         workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr);
 }
 
 int spec_verify(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,

@@ -62,10 +62,10 @@ struct Rows {
 };
 
 template <int DT>
-__device__ inline Rows<DT> decisive_rows(const Params& p, long s, int n) {
+__device__ inline Rows<DT> decisive_rows(const Params& p, long s, const SeqRec& rec) {
   Rows<DT> r;
-  r.rp = row_ptr<DT>(p.lp, s * (p.K + 1) + n, p.V);
-  r.rq = n == p.K ? nullptr : row_ptr<DT>(p.lq, s * p.K + n, p.V);
+  r.rp = row_ptr<DT>(p.lp, s * (p.K + 1) + rec.n, p.V);
+  r.rq = rec.n == rec.kb ? nullptr : row_ptr<DT>(p.lq, s * p.K + rec.n, p.V);
   return r;
 }
 
@@ -384,8 +384,8 @@ __global__ __launch_bounds__(kXBlock) void k_exact_chunks(Params p) {
     const long s = p.queue[p.seq0 + item / p.R3];
     const int r = static_cast<int>(item % p.R3);
     const SeqRec rec = p.rec[s];
-    const bool bonus = rec.n == p.K;
-    exact_chunk_sums<DT, VEC>(p, decisive_rows<DT>(p, s, rec.n), exact_weight(p, rec), bonus, r,
+    const bool bonus = rec.n == rec.kb;
+    exact_chunk_sums<DT, VEC>(p, decisive_rows<DT>(p, s, rec), exact_weight(p, rec), bonus, r,
                               p.xsum + (s * p.R3 + r) * 5);
   }
 }
@@ -396,11 +396,11 @@ __global__ __launch_bounds__(kXBlock) void k_exact_select(Params p) {
   for (long e = blockIdx.x; e < count; e += gridDim.x) {
     const long s = p.queue[p.seq0 + e];
     const SeqRec rec = p.rec[s];
-    const bool bonus = rec.n == p.K;
+    const bool bonus = rec.n == rec.kb;
     __syncthreads();  // shared scalars of the previous entry are no longer read
     int token;
     bool zw_zero;
-    select_exact<DT, VEC>(p, decisive_rows<DT>(p, s, rec.n), exact_weight(p, rec), bonus, p.xsum + s * p.R3 * 5,
+    select_exact<DT, VEC>(p, decisive_rows<DT>(p, s, rec), exact_weight(p, rec), bonus, p.xsum + s * p.R3 * 5,
                           static_cast<double>(p.ur[s]), &token, &zw_zero);
     if (threadIdx.x == 0) {
       p.out_tokens[s * (p.K + 1) + rec.n] = token;

@@ -16,14 +16,15 @@ __global__ __launch_bounds__(kBlock) void k_greedy_scan(Params p) {
   const long s = p.seq0 + blockIdx.x;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int K = p.K, np = p.nch1 * kWaves;
+  const int kb = seq_kb(p, s);  // the sequence's own draft count; rows past it are not read
   __shared__ int sA[SPECV_MAX_K + 1];
   int xk = 0;
   bool valid = true;
-  if (w == 0 && lane < K) {
+  if (w == 0 && lane < kb) {
     xk = p.x[s * K + lane];
     valid = xk >= 0 && xk < p.V;
   }
-  for (int i = w; i <= K; i += kWaves) {
+  for (int i = w; i <= kb; i += kWaves) {
     const float2* pr = p.part + (s * (K + 1) + i) * np;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
@@ -33,13 +34,13 @@ __global__ __launch_bounds__(kBlock) void k_greedy_scan(Params p) {
   }
   __syncthreads();
   if (w != 0) return;
-  const int a = lane <= K ? sA[lane] : 0;
-  const bool match = lane < K && xk == a;
-  const uint64_t lim = (1ull << K) - 1ull;
+  const int a = lane <= kb ? sA[lane] : 0;
+  const bool match = lane < kb && xk == a;
+  const uint64_t lim = (1ull << kb) - 1ull;
   const uint64_t miss = ~static_cast<uint64_t>(__ballot(match)) & lim;
-  const int n = miss ? __ffsll(static_cast<unsigned long long>(miss)) - 1 : K;
+  const int n = miss ? __ffsll(static_cast<unsigned long long>(miss)) - 1 : kb;
   const int an = __shfl(a, n, kWave);
-  const bool bad = n < K && __shfl(valid ? 1 : 0, n, kWave) == 0;
+  const bool bad = n < kb && __shfl(valid ? 1 : 0, n, kWave) == 0;
   if (lane <= K) p.out_tokens[s * (K + 1) + lane] = lane < n ? xk : (lane == n ? an : -1);
   if (lane == 0) {
     p.out_n[s] = n;

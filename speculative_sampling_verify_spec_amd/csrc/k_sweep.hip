@@ -82,12 +82,18 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);
   const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
   const uint32_t row = static_cast<uint32_t>(p.seq0) * (2u * p.K + 1u) + local;
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.qcount[0] = 0u;  // the fp64 draw's queue, filled after this kernel
+  if (p.kb) {  // per-sequence draft counts: rows past a sequence's own are not read
+    const uint32_t per_seq = 2u * p.K + 1u, s = row / per_seq, j = row - s * per_seq;
+    const int kb = seq_kb(p, s);
+    if (j <= static_cast<uint32_t>(p.K) ? j > static_cast<uint32_t>(kb) : j - p.K - 1 >= static_cast<uint32_t>(kb))
+      return;
+  }
   const float c = p.c;
   float e[N];
   uint32_t live;
   long lo, hi;
   load_chunk<DT, VEC>(p, sweep_row<DT>(p, row), chunk, e, live, lo, hi);
-  if (blockIdx.x == 0 && threadIdx.x == 0) p.qcount[0] = 0u;  // the fp64 draw's queue, filled after this kernel
 
   float m = -INFINITY;
 #pragma unroll
@@ -124,6 +130,10 @@ __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
   const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);  // target rows only: s * (K+1) + k
   const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
   const uint32_t row = static_cast<uint32_t>(p.seq0) * (p.K + 1u) + local;
+  if (p.kb) {  // target rows past a sequence's own draft count are not read
+    const uint32_t s = row / (p.K + 1u), j = row - s * (p.K + 1u);
+    if (j > static_cast<uint32_t>(seq_kb(p, s))) return;
+  }
   float e[N];
   uint32_t live;
   long lo, hi;

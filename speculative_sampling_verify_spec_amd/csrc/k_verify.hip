@@ -74,14 +74,17 @@ template <int DT>
 __device__ inline SeqRec accept_scan(const Params& p, long s) {
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int K = p.K, nrows = 2 * K + 1, np = p.nch1 * kWaves;  // kWaves: the sweep's waves per chunk
+  const int kb = seq_kb(p, s);  // the sequence's own draft count
   __shared__ double sL[kRowsMax];  // log2 sum_v 2^(x_v c) of each row
   __shared__ SeqRec sRec;
+  // rows the sequence uses: target rows 0..kb, draft rows 0..kb-1
+  auto used = [&](int i) { return i <= K ? i <= kb : i - K - 1 < kb; };
 
   // wave 0 starts the draft-token gathers at once: they do not need the normalisers
   int xk = 0;
   bool valid = true;
   float xp = 0.f, xq = 0.f;
-  if (w == 0 && lane < K) {
+  if (w == 0 && lane < kb) {
     xk = p.x[s * K + lane];
     valid = xk >= 0 && xk < p.V;
     const int xs = valid ? xk : 0;
@@ -97,7 +100,7 @@ __device__ inline SeqRec accept_scan(const Params& p, long s) {
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
       const int i = w + r * kVWaves;
-      q[r] = (i < nrows && lane < np) ? p.part[(s * nrows + i) * np + lane] : make_float2(-INFINITY, 0.f);
+      q[r] = (i < nrows && used(i) && lane < np) ? p.part[(s * nrows + i) * np + lane] : make_float2(-INFINITY, 0.f);
     }
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
@@ -110,12 +113,13 @@ __device__ inline SeqRec accept_scan(const Params& p, long s) {
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
       const int i = w + r * kVWaves;
-      if (i < nrows) fold_partial(ml[r], sl[r], p.part[(s * nrows + i) * np + j]);
+      if (i < nrows && used(i)) fold_partial(ml[r], sl[r], p.part[(s * nrows + i) * np + j]);
     }
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
     const int i = w + r * kVWaves;
     if (i >= nrows) break;  // uniform over the wave
+    if (!used(i)) continue;
     const double lz2 = wave_log2z(ml[r], sl[r]);
     if (lane == 0) {
       sL[i] = lz2;
@@ -125,25 +129,27 @@ __device__ inline SeqRec accept_scan(const Params& p, long s) {
   __syncthreads();
   if (w == 0) {
     bool accept = false;
-    if (lane < K && valid) {
+    if (lane < kb && valid) {
       const double c = p.c;
       // log2 p(x) - log2 q(x); -inf - -inf gives NaN, which rejects
       const double lr = (static_cast<double>(xp) * c - sL[lane]) - (static_cast<double>(xq) * c - sL[K + 1 + lane]);
       const double thr = lr >= 0.0 ? 1.0 : exp2(lr);
       accept = static_cast<double>(p.ua[s * K + lane]) < thr;
     }
-    const uint64_t lim = (K >= 64) ? ~0ull : ((1ull << K) - 1ull);
+    const uint64_t lim = (kb >= 64) ? ~0ull : ((1ull << kb) - 1ull);
     const uint64_t rejected = ~static_cast<uint64_t>(__ballot(accept)) & lim;
-    const int n = rejected ? __ffsll(static_cast<unsigned long long>(rejected)) - 1 : K;
-    const bool bad = __shfl(valid ? 1 : 0, n < K ? n : 0, kWave) == 0 && n < K;
+    const int n = rejected ? __ffsll(static_cast<unsigned long long>(rejected)) - 1 : kb;
+    const bool bad = __shfl(valid ? 1 : 0, n < kb ? n : 0, kWave) == 0 && n < kb;
     if (lane <= K && lane != n) p.out_tokens[s * (K + 1) + lane] = lane < n ? xk : -1;
     if (lane == 0) {
       p.out_n[s] = n;
       SeqRec r;
       r.n = n;
+      r.kb = kb;
       r.flags = bad ? SPECV_FLAG_BAD_DRAFT : 0;
+      r.pad = 0;
       r.lzp = sL[n];
-      r.lzq = n < K ? sL[K + 1 + n] : 0.0;
+      r.lzq = n < kb ? sL[K + 1 + n] : 0.0;
       p.rec[s] = r;  // read by the fp64 draw if this sequence is queued
       sRec = r;
     }
@@ -468,7 +474,7 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(kVBlock) void k_verify(Params p) {
   const long s = p.seq0 + blockIdx.x;
   const SeqRec rec = accept_scan<DT>(p, s);
-  if (rec.n == p.K) fast_draw<DT, VEC, true>(p, s, rec);
+  if (rec.n == rec.kb) fast_draw<DT, VEC, true>(p, s, rec);
   else fast_draw<DT, VEC, false>(p, s, rec);
 }
 

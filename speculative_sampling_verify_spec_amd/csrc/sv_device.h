@@ -38,6 +38,11 @@ template <> struct Elt<1> {
   }
 };
 
+// Sequence s's draft count: its own (clamped to [0, K]) or K.
+__device__ inline int seq_kb(const Params& p, long s) {
+  return p.kb ? min(max(p.kb[s], 0), p.K) : p.K;
+}
+
 template <int DT>
 __device__ inline const void* row_ptr(const void* base, long row, int V) {
   return static_cast<const char*>(base) + row * static_cast<long>(V) * Elt<DT>::kBytes;

@@ -22,10 +22,12 @@ constexpr int kSweepElems() {
 // Per-sequence record written by the acceptance scan and read by the fp64 draw.
 struct SeqRec {
   int32_t n;       // accepted draft tokens
+  int32_t kb;      // the sequence's draft count (n == kb: bonus draw)
   int32_t flags;   // SPECV_FLAG_* set so far
+  int32_t pad;
   double lzp, lzq; // log2 sum_v 2^(x_v c) of the decisive target / draft row (fp32-accurate)
 };
-static_assert(sizeof(SeqRec) == 24, "SeqRec layout");
+static_assert(sizeof(SeqRec) == 32, "SeqRec layout");
 
 // Constants of the fp64 exp: the Cody-Waite split of ln 2 and the Taylor
 // coefficients 1/n!.  They travel as kernel arguments, so the kernels read
@@ -57,6 +59,8 @@ struct Params {
   const int32_t* x;          // [B][K] draft tokens
   const float* ua;           // [B][K]
   const float* ur;           // [B]
+  const int32_t* kb;         // [B] per-sequence draft counts, or null (all K)
+  unsigned long long* stats; // [2K] per-position counters to add to, or null
   int B, K, V;
   int vec;                   // 1: 16-byte vector loads are legal for every row
   float c;                   // log2(e) / T rounded to fp32
@@ -92,5 +96,6 @@ hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t s, hipEve
 hipError_t launch_verify(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_exact(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_greedy_scan(const Params& p, hipStream_t s);
+hipError_t launch_position_stats(const Params& p, hipStream_t s);
 
 }  // namespace sv

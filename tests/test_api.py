@@ -106,3 +106,22 @@ def test_binding_rejects_host_tensors():
 def test_missing_library_raises(tmp_path):
     with pytest.raises(FileNotFoundError):
         sv.load(str(tmp_path / "nope.so"))
+
+
+def test_ragged_entry_point_checks(lib):
+    KB = 0x90000
+    # num_drafts may not be NULL; otherwise the same host-side checks as spec_verify
+    assert lib.spec_verify_ragged(P, Q, X, None, UA, UR, 1.0, 4, 3, 128, OT, ON, None, F32, WS, 1 << 30, None) == -1
+    assert lib.spec_verify_ragged(P, Q, X, KB, UA, UR, 1.0, 4, 3, 128, OT, ON, None, 7, WS, 1 << 30, None) == -3
+    assert lib.spec_verify_ragged(P, Q, X, KB, UA, UR, -1.0, 4, 3, 128, OT, ON, None, F32, WS, 1 << 30, None) == -4
+    assert lib.spec_verify_ragged(P, Q, X, KB, UA, UR, 1.0, 4, 33, 128, OT, ON, None, F32, WS, 1 << 30, None) == -2
+    assert lib.spec_verify_ragged(P, Q, X, KB, UA, UR, 1.0, 4, 3, 128, OT, ON, None, F32, WS, 16, None) == -5
+    assert lib.spec_verify_ragged(P, None, X, KB, None, None, 0.0, 4, 3, 128, OT, ON, None, F32, WS, 16, None) == -5
+
+
+def test_binding_checks_ragged_arguments():
+    import torch
+    lp = torch.zeros(2, 3, 8)
+    with pytest.raises(ValueError):  # host tensors are refused before anything else
+        sv.verify(lp, torch.zeros(2, 2, 8), torch.zeros(2, 2, dtype=torch.int32), torch.zeros(2, 2),
+                  torch.zeros(2), 1.0, num_drafts=torch.zeros(2, dtype=torch.int32))
