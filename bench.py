@@ -28,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -118,6 +119,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--ragged", action="store_true",
+                    help="per-sequence draft counts K_b uniform on [1, K] (spec_verify_ragged with "
+                         "per-position counters); bytes count the rows actually read")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verify step is data-parallel "
@@ -155,8 +159,17 @@ def main():
     flags = torch.empty((B,), dtype=torch.int32, device="cuda")
     ev = HipEvents(args.steps)
 
+    kb_host = workloads.ragged_draft_counts(B, K) if args.ragged else None
+    if args.ragged:
+        batch = dataclasses.replace(batch, num_drafts=kb_host)  # the oracle baseline verifies the same counts
+    kb = torch.from_numpy(kb_host).cuda() if args.ragged else None
+    stats = torch.zeros(2 * K, dtype=torch.int64, device="cuda")
+
     def step(e=None):
-        rc = sv.spec_verify(lp, lq, x, ua, ur, T, tokens, n_acc, ws, out_flags=flags, events=e, extended=True)
+        if args.ragged:
+            rc = sv.spec_verify_ragged(lp, lq, x, kb, ua, ur, T, tokens, n_acc, ws, position_stats=stats)
+        else:
+            rc = sv.spec_verify(lp, lq, x, ua, ur, T, tokens, n_acc, ws, out_flags=flags, events=e, extended=True)
         if rc != 0:
             raise RuntimeError(sv.strerror(rc))
 
@@ -169,46 +182,53 @@ def main():
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    log(f"timing {args.steps} steps with events on the sweep")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev.pairs[i])
-    torch.cuda.synchronize()
-    wall_ev = time.perf_counter() - t0
-    sweep_ms = [ev.elapsed_ms(i) for i in range(args.steps)]
+    sweep_ms, wall_ev = None, None
+    if not args.ragged:
+        log(f"timing {args.steps} steps with events on the sweep")
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(ev.pairs[i])
+        torch.cuda.synchronize()
+        wall_ev = time.perf_counter() - t0
+        sweep_ms = [ev.elapsed_ms(i) for i in range(args.steps)]
     ev.close()
 
     n_host = n_acc.cpu().numpy()
     tok_host = tokens.cpu().numpy()
-    rows_swept = B * (K + 1) if greedy else B * (2 * K + 1)
+    kbs = kb_host if args.ragged else np.full(B, K)
+    rows_swept = int(np.sum(kbs + 1)) if greedy else int(np.sum(2 * kbs + 1))
     swept = rows_swept * V * elt
-    reread = 0 if greedy else int(np.sum(np.where(n_host < K, 2, 1))) * V * elt
+    reread = 0 if greedy else int(np.sum(np.where(n_host < kbs, 2, 1))) * V * elt
     step_s = wall / args.steps
-    sweep_s = float(np.mean(sweep_ms)) / 1e3
-    achieved = swept / sweep_s / 1e9
-    traffic = counter_traffic(swept)
     line = {
         "metric": "verified seq-steps/s + HBM GB/s (% peak), B=256 K=8 V=128256 bf16",
         "value": B / step_s,
         "unit": "verified seq-steps/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": step_s * 1e3,
-        "ms_per_step_with_events": wall_ev / args.steps * 1e3,
+        "ms_per_step_with_events": None if wall_ev is None else wall_ev / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{wl.name}: verify {wl.describe()}, logits {batch.dtype}",
+        "config": {"workload": f"{wl.name}: verify {wl.describe()}, logits {batch.dtype}"
+                               + (", per-sequence draft counts uniform on [1, K]" if args.ragged else ""),
                    "B": B, "K": K, "V": V, "logits": batch.dtype, "T": T, "parallelism": "none (one GPU)"},
         "hbm_gbps_algorithmic": (swept + reread) / step_s / 1e9,
         "hbm_frac_of_peak": (swept + reread) / step_s / 1e9 / PEAK_HBM_GBS,
         "bytes_per_step": {"swept": swept, "decisive_reread": reread},
         "mean_accepted": float(np.mean(n_host)),
-        "roofline": {"bound": "hbm", "kernel": "sweep_lse" if not greedy else "sweep_argmax",
-                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "launch_us": sweep_s * 1e6, "launches_timed": args.steps,
-                     "algorithmic_bytes_per_launch": swept},
+        "roofline": None,
         "cpu_baseline": None,
     }
+    if args.ragged:
+        line["position_stats"] = stats.cpu().numpy().tolist()
+    else:
+        sweep_s = float(np.mean(sweep_ms)) / 1e3
+        achieved = swept / sweep_s / 1e9
+        line["roofline"] = {"bound": "hbm", "kernel": "sweep_lse" if not greedy else "sweep_argmax",
+                            "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": achieved / PEAK_HBM_GBS, "traffic": counter_traffic(swept),
+                            "launch_us": sweep_s * 1e6, "launches_timed": args.steps,
+                            "algorithmic_bytes_per_launch": swept}
     if not args.no_cpu_baseline:
         log(f"timing the fp64 oracle on a sample (~{args.cpu_seconds:.0f}s)")
         line["cpu_baseline"] = cpu_baseline(batch, tok_host, n_host, args.cpu_seconds)
