@@ -1,4 +1,5 @@
-"""fp64 CPU oracle of the speculative-sampling verify step.
+"""fp64 CPU oracle of the speculative-sampling verify step (and, in
+``oracle.tree``, of greedy token-tree verification and the tree mask).
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the product path.

@@ -105,3 +105,15 @@ def test_generated_shapes(cfg):
     assert b.logits_q.shape == (2, b.K, 2048)
     assert b.draft_tokens.shape == (2, b.K) and b.draft_tokens.dtype == np.int32
     assert np.all((b.draft_tokens >= 0) & (b.draft_tokens < 2048))
+
+
+def test_tree_batches_are_valid_and_deterministic():
+    a = workloads.make_tree_batch(6, 20, 500, "bf16", seed=3, workers=3)
+    b = workloads.make_tree_batch(6, 20, 500, "bf16", seed=3)
+    np.testing.assert_array_equal(a.logits, b.logits)
+    np.testing.assert_array_equal(a.parents, b.parents)
+    np.testing.assert_array_equal(a.tokens, b.tokens)
+    assert np.all(a.parents[:, 0] == -1)
+    v = np.arange(1, 20)
+    assert np.all((a.parents[:, 1:] >= 0) & (a.parents[:, 1:] < v))
+    assert a.logits.dtype == np.uint16 and a.logits.shape == (6, 20, 500)

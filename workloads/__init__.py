@@ -262,6 +262,72 @@ def custom_batch(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: floa
                  u_resample=None if u_resample is None else np.asarray(u_resample, dtype=np.float32).reshape(B))
 
 
+# ------------------------------------------------------------------- trees --
+TREE_STREAM = 100  # seed stream of the token-tree inputs
+
+
+@dataclasses.dataclass
+class TreeBatch:
+    """Token trees in the library's layout: logits [B,N,V] (row v: the
+    target's scores after node v), tokens [B,N] (node 0: the committed root
+    token), parents [B,N] (parents[:, 0] == -1, parents[v] < v)."""
+
+    logits: np.ndarray
+    tokens: np.ndarray
+    parents: np.ndarray
+    dtype: str
+
+    @property
+    def B(self) -> int:
+        return int(self.tokens.shape[0])
+
+    @property
+    def N(self) -> int:
+        return int(self.tokens.shape[1])
+
+    @property
+    def V(self) -> int:
+        return int(self.logits.shape[2])
+
+
+def make_tree(b: int, N: int, V: int, dtype: str, seed: int = DEFAULT_SEED, p_branch: float = 0.5,
+              sigma: float = 2.0, zipf: float = 1.1) -> dict:
+    """Tree ``b``: a chain that branches (node v hangs under a uniformly drawn
+    earlier node with probability p_branch, else under v - 1); every node's
+    row is a Zipf-biased Gaussian row as in the other workloads; node v's
+    token is its parent's first arg-max with probability 1/2, else uniform."""
+    rng = _rng(seed, TREE_STREAM, b)
+    parents = np.empty(N, np.int32)
+    parents[0] = -1
+    for v in range(1, N):
+        parents[v] = rng.integers(0, v) if rng.random() < p_branch else v - 1
+    rows = np.empty((N, V))
+    for v in range(N):
+        rows[v], _ = _zipf_row(rng, V, sigma, zipf)
+    lg = round_logits(rows, dtype)
+    amax = np.argmax(storage_to_f64(lg, dtype), axis=1)
+    tokens = np.empty(N, np.int32)
+    tokens[0] = rng.integers(0, V)
+    take = rng.random(N) < 0.5
+    rand_tok = rng.integers(0, V, size=N)
+    tokens[1:] = np.where(take[1:], amax[parents[1:]], rand_tok[1:])
+    return dict(logits=lg, tokens=tokens, parents=parents)
+
+
+def make_tree_batch(B: int, N: int, V: int, dtype: str, seed: int = DEFAULT_SEED, p_branch: float = 0.5,
+                    workers: int = 1) -> TreeBatch:
+    """B trees of N nodes (see make_tree), generated in threads."""
+    def one(b):
+        return make_tree(b, N, V, dtype, seed, p_branch)
+    if workers > 1 and B > 1:
+        with ThreadPoolExecutor(workers) as ex:
+            trees = list(ex.map(one, range(B)))
+    else:
+        trees = [one(b) for b in range(B)]
+    return TreeBatch(logits=np.stack([t["logits"] for t in trees]), tokens=np.stack([t["tokens"] for t in trees]),
+                     parents=np.stack([t["parents"] for t in trees]), dtype=dtype)
+
+
 def ragged_draft_counts(B: int, K: int, seed: int = DEFAULT_SEED, low: int = 1) -> np.ndarray:
     """Per-sequence draft counts K_b, uniform on [low, K], seeded: the
     stand-in for a proposer that adapts its draft length per sequence."""
