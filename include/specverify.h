@@ -52,6 +52,7 @@ typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype_t;
 #define SPECV_E_HIP        -7   /* a kernel launch failed */
 
 #define SPECV_MAX_K        32   /* one 64-lane wave runs the acceptance scan */
+#define SPECV_MAX_TREE     64   /* token-tree nodes: one per lane of a wave */
 
 /* Flag bits of out_flags (bit 0 is unused). */
 #define SPECV_FLAG_ZW_ZERO   2  /* residual mass was zero after rounding; drew from p_n instead */
@@ -154,6 +155,48 @@ int spec_verify_ragged(const void* logits_p, const void* logits_q, const int32_t
                        int B, int K, int V, int32_t* out_tokens, int32_t* out_n_accepted,
                        uint64_t* position_stats, int dtype, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * Token trees ([A] "Token tree: kiểm nhiều nhánh đoán cùng lúc"; [C] sections
+ * 3.1, 3.2, 8 and 9.1).  A tree of N nodes (1 <= N <= SPECV_MAX_TREE) is
+ * parents [N] int32 with parents[0] == -1 (node 0, the root, holds the last
+ * committed token) and parents[v] < v, plus a token per node; row v of the
+ * logits scores the token after node v.  A node whose parent is not in
+ * [0, v) sees only itself, has depth 0 and is never accepted.
+ *
+ * spec_verify_tree_greedy - greedy verification of B trees.  Node v is
+ * accepted when its parent is and its token is the first arg-max of its
+ * parent's row; the round's output is the path from the root to the deepest
+ * accepted node d (the lowest index among equally deep ones), then the
+ * first arg-max of row d ([A]: the deepest accepted branch is the output;
+ * [C] 9.1: greedy matching, which is exact for T = 0).
+ *   logits         [B][N][V] target logits (dtype), aligned to the element size
+ *   tree_tokens    [B][N] int32; parents [B][N] int32
+ *   out_tokens     [B][N] int32: the path's tokens after the root, the bonus
+ *                  token, then -1
+ *   out_path       [B][N] int32 or NULL: node indices of the path (root
+ *                  first), then -1 (which nodes' cache entries to keep)
+ *   out_n_accepted [B] int32: accepted drafts = depth of d
+ *   workspace      spec_verify_tree_workspace_size() bytes, 256-byte aligned
+ * Returns the SPECV_* codes of spec_verify; nothing synchronises.
+ */
+size_t spec_verify_tree_workspace_size(int B, int N, int V, int dtype);
+
+int spec_verify_tree_greedy(const void* logits, const int32_t* tree_tokens, const int32_t* parents, int B, int N,
+                            int V, int32_t* out_tokens, int32_t* out_path, int32_t* out_n_accepted, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_tree_mask - the tree attention mask and depth position ids of B trees
+ * ([C] 3.1: a node sees the shared prefix and its own ancestors only; 3.2:
+ * its position id is its depth; 8: worked example).
+ *   parents   [B][N] int32 (device)
+ *   out_mask  [B][N][N] uint8 or NULL: out_mask[b][i][j] = 1 when node i may
+ *             attend to node j (j is i or an ancestor of i), else 0
+ *   out_depth [B][N] int32 or NULL: depth of every node (root 0)
+ * At least one output must be given.  Needs no workspace.
+ */
+int spec_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int32_t* out_depth, void* stream);
 
 /* Static description of a return code. */
 const char* spec_verify_strerror(int code);

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(PKG, "libspecverify.so")
 
 SPECV_F32, SPECV_BF16 = 0, 1
 SPECV_MAX_K = 32
+SPECV_MAX_TREE = 64
 FLAG_ZW_ZERO, FLAG_BAD_DRAFT = 2, 4
 
 ERRORS = {0: "SPECV_OK", -1: "SPECV_E_NULL", -2: "SPECV_E_SHAPE", -3: "SPECV_E_DTYPE", -4: "SPECV_E_TEMP",
@@ -23,6 +24,7 @@ ERRORS = {0: "SPECV_OK", -1: "SPECV_E_NULL", -2: "SPECV_E_SHAPE", -3: "SPECV_E_D
 
 # every symbol include/specverify.h declares
 EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_ex", "spec_verify_ragged",
+           "spec_verify_tree_workspace_size", "spec_verify_tree_greedy", "spec_tree_mask",
            "spec_verify_strerror", "spec_verify_version")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -56,6 +58,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_ex.restype = i32
     lib.spec_verify_ragged.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
     lib.spec_verify_ragged.restype = i32
+    lib.spec_verify_tree_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.spec_verify_tree_workspace_size.restype = sz
+    lib.spec_verify_tree_greedy.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
+    lib.spec_verify_tree_greedy.restype = i32
+    lib.spec_tree_mask.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.spec_tree_mask.restype = i32
     lib.spec_verify_strerror.argtypes = [i32]
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     lib.spec_verify_version.argtypes = []
@@ -199,3 +207,54 @@ def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
     if return_flags:
         out += (flags,)
     return out
+
+
+def verify_tree_greedy(logits, tree_tokens, parents, *, workspace=None):
+    """Greedy verification of B token trees on torch device tensors.
+
+    logits [B,N,V] (bf16 or fp32), tree_tokens and parents [B,N] int32, all
+    contiguous on one device.  Returns (tokens [B,N], path [B,N],
+    n_accepted [B]) as int32 device tensors; nothing synchronises."""
+    import torch
+    dev = logits.device
+    if dev.type != "cuda" or logits.dim() != 3:
+        raise ValueError("logits must be a [B, N, V] device tensor")
+    B, N, V = logits.shape
+    for t in (tree_tokens, parents):
+        if t.device != dev or t.dtype != torch.int32 or tuple(t.shape) != (B, N) or not t.is_contiguous():
+            raise ValueError("tree_tokens and parents must be contiguous int32 [B, N] on the logits' device")
+    if not logits.is_contiguous():
+        raise ValueError("logits must be contiguous")
+    dt = _dtype_code(logits)
+    need = int(load().spec_verify_tree_workspace_size(B, N, V, dt))
+    if need == 0:
+        raise SpecVerifyError(-2, "invalid tree shape")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    rc = int(load().spec_verify_tree_greedy(_ptr(logits), _ptr(tree_tokens), _ptr(parents), B, N, V, _ptr(tokens),
+                                            _ptr(path), _ptr(n_acc), dt, _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), st))
+    if rc != 0:
+        raise SpecVerifyError(rc, strerror(rc))
+    return tokens, path, n_acc
+
+
+def tree_mask(parents):
+    """Tree attention mask [B,N,N] uint8 and depth position ids [B,N] int32
+    of B trees given by parents [B,N] int32 (a device tensor)."""
+    import torch
+    if parents.device.type != "cuda" or parents.dtype != torch.int32 or parents.dim() != 2 or \
+            not parents.is_contiguous():
+        raise ValueError("parents must be a contiguous int32 [B, N] device tensor")
+    B, N = parents.shape
+    mask = torch.empty((B, N, N), dtype=torch.uint8, device=parents.device)
+    depth = torch.empty((B, N), dtype=torch.int32, device=parents.device)
+    st = torch.cuda.current_stream(parents.device).cuda_stream
+    rc = int(load().spec_tree_mask(_ptr(parents), B, N, _ptr(mask), _ptr(depth), st))
+    if rc != 0:
+        raise SpecVerifyError(rc, strerror(rc))
+    return mask, depth

@@ -204,11 +204,82 @@ int spec_verify(const void* logits_p, const void* logits_q, const int32_t* draft
                         nullptr);
 }
 
+namespace sv {
+namespace {
+
+bool valid_tree_shape(int B, int N, int V) {
+  if (B < 1 || N < 1 || N > SPECV_MAX_TREE || V < 1) return false;
+  const long nch_max = (static_cast<long>(V) + kBlock * 16 - 1) / (kBlock * 16);
+  if (static_cast<long>(B) * N * nch_max >= (1L << 31)) return false;
+  return static_cast<double>(B) * N * V * 4.0 <= 9.0e18;
+}
+
+size_t tree_workspace(int B, int N, int V, int dtype) {
+  const size_t a = make_layout(B, N - 1, V, dtype, false, true).total;
+  const size_t b = make_layout(B, N - 1, V, dtype, true, true).total;
+  return a > b ? a : b;
+}
+
+}  // namespace
+}  // namespace sv
+
+size_t spec_verify_tree_workspace_size(int B, int N, int V, int dtype) {
+  if (dtype != SPECV_F32 && dtype != SPECV_BF16) return 0;
+  if (!sv::valid_tree_shape(B, N, V)) return 0;
+  return sv::tree_workspace(B, N, V, dtype);
+}
+
+int spec_verify_tree_greedy(const void* logits, const int32_t* tree_tokens, const int32_t* parents, int B, int N,
+                            int V, int32_t* out_tokens, int32_t* out_path, int32_t* out_n_accepted, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace sv;
+  if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_E_DTYPE;
+  if (!logits || !tree_tokens || !parents || !out_tokens || !out_n_accepted) return SPECV_E_NULL;
+  if (!valid_tree_shape(B, N, V)) return SPECV_E_SHAPE;
+  const uintptr_t eb = static_cast<uintptr_t>(elt_bytes(dtype));
+  const uintptr_t ap = reinterpret_cast<uintptr_t>(logits);
+  if (ap % eb) return SPECV_E_ALIGN;
+  const bool vec = ap % 16 == 0 && (static_cast<long>(V) * eb) % 16 == 0;
+  const Layout L = make_layout(B, N - 1, V, dtype, vec, true);
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign || workspace_bytes < L.total)
+    return SPECV_E_WORKSPACE;
+  Params P{};
+  P.lp = logits;
+  P.x = tree_tokens;
+  P.parents = parents;
+  P.out_path = out_path;
+  P.B = B;
+  P.K = N - 1;
+  P.V = V;
+  P.vec = vec ? 1 : 0;
+  P.out_tokens = out_tokens;
+  P.out_n = out_n_accepted;
+  P.part = reinterpret_cast<float2*>(static_cast<char*>(workspace) + L.part);
+  P.seq0 = 0;
+  P.nseq = B;
+  P.nch1 = L.nch1;
+  P.ch1 = L.ch1;
+  P.cq = L.cq;
+  P.cr = L.cr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (launch_sweep_argmax(P, dtype, st, nullptr, nullptr) != hipSuccess) return SPECV_E_HIP;
+  if (launch_tree_scan(P, st) != hipSuccess) return SPECV_E_HIP;
+  return SPECV_OK;
+}
+
+int spec_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int32_t* out_depth, void* stream) {
+  if (!parents || (!out_mask && !out_depth)) return SPECV_E_NULL;
+  if (B < 1 || N < 1 || N > SPECV_MAX_TREE || static_cast<long>(B) * N * N >= (1L << 40)) return SPECV_E_SHAPE;
+  if (sv::launch_tree_mask(parents, B, N, out_mask, out_depth, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SPECV_E_HIP;
+  return SPECV_OK;
+}
+
 const char* spec_verify_strerror(int code) {
   switch (code) {
     case SPECV_OK: return "ok";
     case SPECV_E_NULL: return "a required pointer is NULL";
-    case SPECV_E_SHAPE: return "invalid shape (B >= 1, 1 <= K <= 32, V >= 1, sizes in range)";
+    case SPECV_E_SHAPE: return "invalid shape (B >= 1, 1 <= K <= 32 or 1 <= N <= 64 tree nodes, V >= 1, sizes in range)";
     case SPECV_E_DTYPE: return "dtype must be SPECV_F32 or SPECV_BF16";
     case SPECV_E_TEMP: return "T must be 0 (greedy) or finite and > 0 with 1/T finite";
     case SPECV_E_WORKSPACE: return "workspace NULL, not 256-byte aligned, or too small";

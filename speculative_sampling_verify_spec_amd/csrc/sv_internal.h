@@ -60,6 +60,8 @@ struct Params {
   const float* ua;           // [B][K]
   const float* ur;           // [B]
   const int32_t* kb;         // [B] per-sequence draft counts, or null (all K)
+  const int32_t* parents;    // token trees: [B][N] parent of each node (x holds the node tokens, K = N - 1)
+  int32_t* out_path;         // token trees: [B][N] node indices of the accepted path, or null
   unsigned long long* stats; // [2K] per-position counters to add to, or null
   int B, K, V;
   int vec;                   // 1: 16-byte vector loads are legal for every row
@@ -97,5 +99,8 @@ hipError_t launch_verify(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_exact(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_greedy_scan(const Params& p, hipStream_t s);
 hipError_t launch_position_stats(const Params& p, hipStream_t s);
+hipError_t launch_tree_scan(const Params& p, hipStream_t s);
+hipError_t launch_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int32_t* out_depth,
+                            hipStream_t s);
 
 }  // namespace sv

@@ -21,7 +21,7 @@ def lib():
 
 def test_header_declarations_are_all_exported(lib):
     text = open(HEADER).read()
-    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(spec_verify\w*)\s*\(", text, re.M))
+    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(spec_\w+)\s*\(", text, re.M))
     assert declared == set(sv.EXPORTS), declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -31,6 +31,7 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     consts = dict((k, int(v)) for k, v in re.findall(r"#define\s+(SPECV_\w+)\s+(-?\d+)", text))
     assert consts["SPECV_MAX_K"] == sv.SPECV_MAX_K
+    assert consts["SPECV_MAX_TREE"] == sv.SPECV_MAX_TREE
     assert consts["SPECV_FLAG_ZW_ZERO"] == sv.FLAG_ZW_ZERO and consts["SPECV_FLAG_BAD_DRAFT"] == sv.FLAG_BAD_DRAFT
     for code, name in sv.ERRORS.items():
         assert consts.get(name, 0) == code, name
@@ -125,3 +126,21 @@ def test_binding_checks_ragged_arguments():
     with pytest.raises(ValueError):  # host tensors are refused before anything else
         sv.verify(lp, torch.zeros(2, 2, 8), torch.zeros(2, 2, dtype=torch.int32), torch.zeros(2, 2),
                   torch.zeros(2), 1.0, num_drafts=torch.zeros(2, dtype=torch.int32))
+
+
+def test_tree_entry_points_check_arguments(lib):
+    L, TT, PA, OTT, OP, ONN = (0x100000 * i for i in range(1, 7))
+    assert lib.spec_verify_tree_workspace_size(4, 16, 1000, BF16) > 0
+    for bad in [(0, 16, 1000, BF16), (4, 0, 1000, BF16), (4, 65, 1000, BF16), (4, 16, 0, BF16), (4, 16, 1000, 9)]:
+        assert lib.spec_verify_tree_workspace_size(*bad) == 0, bad
+    call = lambda **k: lib.spec_verify_tree_greedy(k.get("l", L), k.get("tt", TT), k.get("pa", PA), k.get("B", 4),
+                                                     k.get("N", 16), k.get("V", 1000), OTT, OP, ONN,
+                                                     k.get("dt", BF16), k.get("ws", WS), k.get("wsb", 1 << 30), None)
+    assert call(dt=5) == -3
+    assert call(l=None) == -1 and call(pa=None) == -1 and call(tt=None) == -1
+    assert call(N=65) == -2 and call(N=0) == -2 and call(B=0) == -2
+    assert call(l=L + 1) == -6
+    assert call(wsb=64) == -5 and call(ws=None) == -5
+    assert lib.spec_tree_mask(None, 4, 16, OTT, OP, None) == -1
+    assert lib.spec_tree_mask(PA, 4, 16, None, None, None) == -1
+    assert lib.spec_tree_mask(PA, 4, 65, OTT, OP, None) == -2

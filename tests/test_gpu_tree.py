@@ -1,0 +1,91 @@
+"""GPU parity of token-tree verification (greedy) and of the tree attention
+mask / depth position ids, against the CPU oracle in oracle.tree."""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import tree
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _logits_dev(tb):
+    import torch
+    if tb.dtype == "bf16":
+        return _dev(tb.logits.view(np.int16)).view(torch.bfloat16)
+    return _dev(tb.logits)
+
+
+@pytest.mark.parametrize("B,N,V,dt,pb", [(8, 1, 1000, "bf16", 0.5), (16, 5, 777, "fp32", 0.5),
+                                         (32, 32, 32000, "bf16", 0.5), (8, 64, 5001, "fp32", 0.3),
+                                         (12, 64, 128256, "bf16", 0.7), (6, 17, 999, "bf16", 1.0)],
+                         ids=lambda x: str(x))
+def test_tree_verification_matches_oracle(gpu_lib, B, N, V, dt, pb):
+    import torch
+    tb = workloads.make_tree_batch(B, N, V, dt, seed=N + V, p_branch=pb, workers=workloads.default_workers())
+    say(f"[tree] B={B} N={N} V={V} {dt} p_branch={pb}")
+    tok, path, n = gpu_lib.verify_tree_greedy(_logits_dev(tb), _dev(tb.tokens), _dev(tb.parents))
+    torch.cuda.synchronize()
+    rt, rp, rn = tree.verify_tree_greedy(tb.logits, tb.tokens, tb.parents, tb.dtype)
+    np.testing.assert_array_equal(n.cpu().numpy(), rn)
+    np.testing.assert_array_equal(tok.cpu().numpy(), rt)
+    np.testing.assert_array_equal(path.cpu().numpy(), rp)
+
+
+@pytest.mark.parametrize("N", [1, 2, 5, 33, 64])
+def test_tree_mask_matches_oracle(gpu_lib, N):
+    import torch
+    rng = np.random.default_rng(N)
+    B = 20
+    parents = np.stack([np.concatenate([[-1], [rng.integers(0, v) if rng.random() < 0.5 else v - 1
+                                               for v in range(1, N)]]) for _ in range(B)]).astype(np.int32)
+    parents[3, N // 2] = N + 7 if N > 2 else parents[3, N // 2]      # invalid parents: see only themselves
+    parents[4, N - 1] = -5 if N > 1 else parents[4, N - 1]
+    mask, depth = gpu_lib.tree_mask(_dev(parents))
+    torch.cuda.synchronize()
+    mask, depth = mask.cpu().numpy(), depth.cpu().numpy()
+    for b in range(B):
+        m, d = tree.tree_mask(parents[b])
+        np.testing.assert_array_equal(mask[b], m)
+        np.testing.assert_array_equal(depth[b], d)
+
+
+def test_tree_with_invalid_parents_matches_oracle(gpu_lib):
+    import torch
+    tb = workloads.make_tree_batch(16, 24, 3000, "fp32", seed=5, workers=workloads.default_workers())
+    parents = tb.parents.copy()
+    parents[::3, 7] = 30
+    parents[1::3, 11] = -2
+    tok, path, n = gpu_lib.verify_tree_greedy(_logits_dev(tb), _dev(tb.tokens), _dev(parents))
+    torch.cuda.synchronize()
+    rt, rp, rn = tree.verify_tree_greedy(tb.logits, tb.tokens, parents, tb.dtype)
+    np.testing.assert_array_equal(n.cpu().numpy(), rn)
+    np.testing.assert_array_equal(tok.cpu().numpy(), rt)
+    np.testing.assert_array_equal(path.cpu().numpy(), rp)
+
+
+def test_chain_tree_equals_the_linear_greedy_entry_point(gpu_lib):
+    """A chain tree of K+1 nodes is linear greedy verification: the same
+    accepted counts and tokens as spec_verify at T = 0."""
+    import torch
+    b = workloads.make_batch(4, seqs=range(48), workers=workloads.default_workers())
+    lp, _, x, _, _ = workloads.to_device(b)
+    tok_lin, n_lin = gpu_lib.verify(lp, None, x, None, None, 0.0)
+    K = b.K
+    tokens = torch.cat([torch.zeros((b.B, 1), dtype=torch.int32, device="cuda"), x], dim=1).contiguous()
+    parents = torch.arange(-1, K, dtype=torch.int32, device="cuda").expand(b.B, K + 1).contiguous()
+    tok_t, path, n_t = gpu_lib.verify_tree_greedy(lp, tokens, parents)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(n_t.cpu().numpy(), n_lin.cpu().numpy())
+    np.testing.assert_array_equal(tok_t.cpu().numpy(), tok_lin.cpu().numpy())
