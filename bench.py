@@ -110,6 +110,54 @@ def cpu_baseline(batch, gpu_tokens, gpu_n, budget_s: float):
             "sample_compared": min(done, batch.B)}
 
 
+def tree_bench(args):
+    """Greedy token-tree verification: B trees of N nodes over V=128256 bf16
+    logits (every node's row read once)."""
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verify_spec_amd as sv
+    import workloads
+    B, N, V = 128, 32, 128256
+    log(f"generating {B} trees of {N} nodes, V={V} bf16")
+    tb = workloads.make_tree_batch(B, N, V, "bf16", workers=workloads.default_workers())
+    lg = torch.from_numpy(tb.logits.view(np.int16)).cuda().view(torch.bfloat16)
+    tok_in = torch.from_numpy(tb.tokens).cuda()
+    par = torch.from_numpy(tb.parents).cuda()
+    ws = torch.empty(int(sv.load().spec_verify_tree_workspace_size(B, N, V, sv.SPECV_BF16)), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(args.warmup):
+        out = sv.verify_tree_greedy(lg, tok_in, par, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        out = sv.verify_tree_greedy(lg, tok_in, par, workspace=ws)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    n = out[2].cpu().numpy()
+    nbytes = B * N * V * 2
+    line = {"metric": "verified trees/s + HBM GB/s (% peak), greedy token trees", "value": B / step_s,
+            "unit": "verified trees/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"tree-bf16: {B} trees of {N} nodes (chains branching with probability 1/2), "
+                                   f"V={V} bf16, greedy", "B": B, "N": N, "V": V},
+            "hbm_gbps_algorithmic": nbytes / step_s / 1e9, "hbm_frac_of_peak": nbytes / step_s / 1e9 / PEAK_HBM_GBS,
+            "bytes_per_step": nbytes, "mean_accepted": float(np.mean(n)), "roofline": None, "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        from oracle import tree
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds or done == 0:
+            b = done % B
+            tree.verify_tree_greedy_sequence(tb.logits[b], tb.tokens[b], tb.parents[b], "bf16")
+            done += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": done / dt, "unit": "verified trees/s", "cores": 1, "kind": "oracle",
+                                "sample": f"{done} tree verifications of the timed batch, numpy, one thread",
+                                "seconds": round(dt, 2)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +167,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--tree", action="store_true",
+                    help="greedy token-tree verification: 128 trees of 32 nodes, V=128256 bf16")
     ap.add_argument("--ragged", action="store_true",
                     help="per-sequence draft counts K_b uniform on [1, K] (spec_verify_ragged with "
                          "per-position counters); bytes count the rows actually read")
@@ -135,6 +185,9 @@ def main():
     import workloads
 
     sv.load()
+    if args.tree:
+        tree_bench(args)
+        return
     if args.copy_calibration > 0:
         src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
