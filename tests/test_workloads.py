@@ -117,3 +117,17 @@ def test_tree_batches_are_valid_and_deterministic():
     v = np.arange(1, 20)
     assert np.all((a.parents[:, 1:] >= 0) & (a.parents[:, 1:] < v))
     assert a.logits.dtype == np.uint16 and a.logits.shape == (6, 20, 500)
+
+
+def test_histories_are_deterministic_and_self_similar():
+    h1, n1 = workloads.make_histories(8, 2000, 32000, seed=4, workers=4)
+    h2, n2 = workloads.make_histories(8, 2000, 32000, seed=4)
+    np.testing.assert_array_equal(h1, h2)
+    np.testing.assert_array_equal(n1, n2)
+    assert np.all((n1 >= 1000) & (n1 <= 2000))
+    for b in range(8):
+        assert np.all(h1[b, n1[b]:] == -1) and np.all((h1[b, : n1[b]] >= 0) & (h1[b, : n1[b]] < 32000))
+    # copies make repeated 4-grams common
+    h = h1[0, : n1[0]]
+    grams = {tuple(h[i:i + 4]) for i in range(len(h) - 3)}
+    assert len(grams) < 0.9 * (len(h) - 3)

@@ -328,6 +328,50 @@ def make_tree_batch(B: int, N: int, V: int, dtype: str, seed: int = DEFAULT_SEED
                      parents=np.stack([t["parents"] for t in trees]), dtype=dtype)
 
 
+# --------------------------------------------------------------- histories --
+HISTORY_STREAM = 200  # seed stream of the token histories
+
+
+def make_history(b: int, L: int, vocab: int, seed: int = DEFAULT_SEED, p_copy: float = 0.5) -> np.ndarray:
+    """Token history ``b`` of length uniform in [L/2, L]: alternating spans of
+    fresh tokens (Zipf-distributed ranks over a seeded vocabulary permutation,
+    mean span 8) and, with probability p_copy, copies of an earlier span (mean
+    length 16), the self-similarity of edited code and templates that n-gram
+    proposers feed on."""
+    rng = _rng(seed, HISTORY_STREAM, b)
+    n = int(rng.integers(max(1, L // 2), L + 1))
+    perm = rng.permutation(vocab)
+    out = np.empty(n, np.int64)
+    m = 0
+    while m < n:
+        if m > 16 and rng.random() < p_copy:
+            start = int(rng.integers(0, m - 1))
+            span = min(int(rng.geometric(1 / 16)), m - start, n - m)
+            out[m:m + span] = out[start:start + span]
+        else:
+            span = min(int(rng.geometric(1 / 8)), n - m)
+            ranks = np.minimum(rng.zipf(1.2, size=span) - 1, vocab - 1)
+            out[m:m + span] = perm[ranks]
+        m += span
+    return out.astype(np.int32)
+
+
+def make_histories(B: int, L: int, vocab: int, seed: int = DEFAULT_SEED, p_copy: float = 0.5,
+                   workers: int = 1):
+    """B histories padded with -1 to [B, L] int32, and their lengths [B]."""
+    def one(b):
+        return make_history(b, L, vocab, seed, p_copy)
+    if workers > 1 and B > 1:
+        with ThreadPoolExecutor(workers) as ex:
+            hs = list(ex.map(one, range(B)))
+    else:
+        hs = [one(b) for b in range(B)]
+    out = np.full((B, L), -1, np.int32)
+    for b, h in enumerate(hs):
+        out[b, : len(h)] = h
+    return out, np.array([len(h) for h in hs], np.int32)
+
+
 def ragged_draft_counts(B: int, K: int, seed: int = DEFAULT_SEED, low: int = 1) -> np.ndarray:
     """Per-sequence draft counts K_b, uniform on [low, K], seeded: the
     stand-in for a proposer that adapts its draft length per sequence."""
