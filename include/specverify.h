@@ -53,6 +53,7 @@ typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype_t;
 
 #define SPECV_MAX_K        32   /* one 64-lane wave runs the acceptance scan */
 #define SPECV_MAX_TREE     64   /* token-tree nodes: one per lane of a wave */
+#define SPECV_MAX_NGRAM    16   /* largest n-gram the prompt-lookup proposer matches */
 
 /* Flag bits of out_flags (bit 0 is unused). */
 #define SPECV_FLAG_ZW_ZERO   2  /* residual mass was zero after rounding; drew from p_n instead */
@@ -197,6 +198,26 @@ int spec_verify_tree_greedy(const void* logits, const int32_t* tree_tokens, cons
  * At least one output must be given.  Needs no workspace.
  */
 int spec_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int32_t* out_depth, void* stream);
+
+/*
+ * spec_ngram_propose - n-gram (prompt-lookup) drafts from the token history
+ * of B sequences ([D] "Спекулятивное декодирование на n-граммах": when the
+ * latest tokens repeat an earlier n-gram, propose what followed it, with an
+ * n-gram size and a minimum number of hits; [A]: Prompt Lookup, drafts taken
+ * from the context).  For sizes n = n_max down to n_min, an occurrence of the
+ * history's last n tokens ends at e (1 <= e <= L - 1: a token follows it);
+ * the largest n with at least min_hits occurrences wins, and the draft is
+ * the K tokens after its latest occurrence, cut at the end of the history.
+ *   history   [B][L_max] int32 (device), row b valid for its first lengths[b]
+ *   lengths   [B] int32 (device), clamped to [0, L_max]
+ *   n_min, n_max   1 <= n_min <= n_max <= SPECV_MAX_NGRAM
+ *   min_hits  >= 1;  K  1 <= K <= SPECV_MAX_K
+ *   out_draft [B][K] int32: the draft, then -1;  out_count [B] int32: its length (0: none)
+ * Returns SPECV_OK, SPECV_E_NULL or SPECV_E_SHAPE (any size out of range);
+ * needs no workspace; nothing synchronises.
+ */
+int spec_ngram_propose(const int32_t* history, const int32_t* lengths, int B, int L_max, int n_min, int n_max,
+                       int min_hits, int K, int32_t* out_draft, int32_t* out_count, void* stream);
 
 /* Static description of a return code. */
 const char* spec_verify_strerror(int code);

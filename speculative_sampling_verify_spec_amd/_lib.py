@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libspecverify.so")
 SPECV_F32, SPECV_BF16 = 0, 1
 SPECV_MAX_K = 32
 SPECV_MAX_TREE = 64
+SPECV_MAX_NGRAM = 16
 FLAG_ZW_ZERO, FLAG_BAD_DRAFT = 2, 4
 
 ERRORS = {0: "SPECV_OK", -1: "SPECV_E_NULL", -2: "SPECV_E_SHAPE", -3: "SPECV_E_DTYPE", -4: "SPECV_E_TEMP",
@@ -24,7 +25,7 @@ ERRORS = {0: "SPECV_OK", -1: "SPECV_E_NULL", -2: "SPECV_E_SHAPE", -3: "SPECV_E_D
 
 # every symbol include/specverify.h declares
 EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_ex", "spec_verify_ragged",
-           "spec_verify_tree_workspace_size", "spec_verify_tree_greedy", "spec_tree_mask",
+           "spec_verify_tree_workspace_size", "spec_verify_tree_greedy", "spec_tree_mask", "spec_ngram_propose",
            "spec_verify_strerror", "spec_verify_version")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -64,6 +65,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_tree_greedy.restype = i32
     lib.spec_tree_mask.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.spec_tree_mask.restype = i32
+    lib.spec_ngram_propose.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.spec_ngram_propose.restype = i32
     lib.spec_verify_strerror.argtypes = [i32]
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     lib.spec_verify_version.argtypes = []
@@ -258,3 +261,24 @@ def tree_mask(parents):
     if rc != 0:
         raise SpecVerifyError(rc, strerror(rc))
     return mask, depth
+
+
+def ngram_propose(history, lengths, n_min: int, n_max: int, min_hits: int, K: int):
+    """Prompt-lookup drafts for B token histories (device tensors: history
+    [B, L_max] int32 padded, lengths [B] int32).  Returns (draft [B, K],
+    count [B]) int32 device tensors; nothing synchronises."""
+    import torch
+    dev = history.device
+    if dev.type != "cuda" or history.dtype != torch.int32 or history.dim() != 2 or not history.is_contiguous():
+        raise ValueError("history must be a contiguous int32 [B, L_max] device tensor")
+    B, L = history.shape
+    if lengths.device != dev or lengths.dtype != torch.int32 or tuple(lengths.shape) != (B,):
+        raise ValueError("lengths must be an int32 [B] tensor on the history's device")
+    draft = torch.empty((B, K), dtype=torch.int32, device=dev)
+    count = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    rc = int(load().spec_ngram_propose(_ptr(history), _ptr(lengths), B, L, n_min, n_max, min_hits, K, _ptr(draft),
+                                       _ptr(count), st))
+    if rc != 0:
+        raise SpecVerifyError(rc, strerror(rc))
+    return draft, count

@@ -267,6 +267,18 @@ int spec_verify_tree_greedy(const void* logits, const int32_t* tree_tokens, cons
   return SPECV_OK;
 }
 
+int spec_ngram_propose(const int32_t* history, const int32_t* lengths, int B, int L_max, int n_min, int n_max,
+                       int min_hits, int K, int32_t* out_draft, int32_t* out_count, void* stream) {
+  if (!history || !lengths || !out_draft || !out_count) return SPECV_E_NULL;
+  if (B < 1 || L_max < 1 || n_min < 1 || n_max < n_min || n_max > SPECV_MAX_NGRAM || min_hits < 1 || K < 1 ||
+      K > SPECV_MAX_K)
+    return SPECV_E_SHAPE;
+  if (sv::launch_ngram(history, lengths, B, L_max, n_min, n_max, min_hits, K, out_draft, out_count,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SPECV_E_HIP;
+  return SPECV_OK;
+}
+
 int spec_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int32_t* out_depth, void* stream) {
   if (!parents || (!out_mask && !out_depth)) return SPECV_E_NULL;
   if (B < 1 || N < 1 || N > SPECV_MAX_TREE || static_cast<long>(B) * N * N >= (1L << 40)) return SPECV_E_SHAPE;
@@ -279,7 +291,7 @@ const char* spec_verify_strerror(int code) {
   switch (code) {
     case SPECV_OK: return "ok";
     case SPECV_E_NULL: return "a required pointer is NULL";
-    case SPECV_E_SHAPE: return "invalid shape (B >= 1, 1 <= K <= 32 or 1 <= N <= 64 tree nodes, V >= 1, sizes in range)";
+    case SPECV_E_SHAPE: return "invalid shape or size (B >= 1, 1 <= K <= 32, 1 <= N <= 64 tree nodes, 1 <= n <= 16 n-gram sizes, V >= 1, sizes in range)";
     case SPECV_E_DTYPE: return "dtype must be SPECV_F32 or SPECV_BF16";
     case SPECV_E_TEMP: return "T must be 0 (greedy) or finite and > 0 with 1/T finite";
     case SPECV_E_WORKSPACE: return "workspace NULL, not 256-byte aligned, or too small";

@@ -100,6 +100,8 @@ hipError_t launch_exact(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_greedy_scan(const Params& p, hipStream_t s);
 hipError_t launch_position_stats(const Params& p, hipStream_t s);
 hipError_t launch_tree_scan(const Params& p, hipStream_t s);
+hipError_t launch_ngram(const int32_t* hist, const int32_t* lengths, int B, int Lmax, int n_min, int n_max,
+                        int min_hits, int K, int32_t* out_draft, int32_t* out_count, hipStream_t s);
 hipError_t launch_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int32_t* out_depth,
                             hipStream_t s);
 

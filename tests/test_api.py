@@ -32,6 +32,7 @@ def test_header_constants_match_binding():
     consts = dict((k, int(v)) for k, v in re.findall(r"#define\s+(SPECV_\w+)\s+(-?\d+)", text))
     assert consts["SPECV_MAX_K"] == sv.SPECV_MAX_K
     assert consts["SPECV_MAX_TREE"] == sv.SPECV_MAX_TREE
+    assert consts["SPECV_MAX_NGRAM"] == sv.SPECV_MAX_NGRAM
     assert consts["SPECV_FLAG_ZW_ZERO"] == sv.FLAG_ZW_ZERO and consts["SPECV_FLAG_BAD_DRAFT"] == sv.FLAG_BAD_DRAFT
     for code, name in sv.ERRORS.items():
         assert consts.get(name, 0) == code, name
@@ -144,3 +145,14 @@ def test_tree_entry_points_check_arguments(lib):
     assert lib.spec_tree_mask(None, 4, 16, OTT, OP, None) == -1
     assert lib.spec_tree_mask(PA, 4, 16, None, None, None) == -1
     assert lib.spec_tree_mask(PA, 4, 65, OTT, OP, None) == -2
+
+
+def test_ngram_entry_point_checks_arguments(lib):
+    H, LN, D, C = (0x100000 * i for i in range(1, 5))
+    call = lambda **k: lib.spec_ngram_propose(k.get("h", H), k.get("ln", LN), k.get("B", 4), k.get("L", 100),
+                                               k.get("nmin", 1), k.get("nmax", 4), k.get("hits", 1), k.get("K", 5),
+                                               k.get("d", D), k.get("c", C), None)
+    assert call(h=None) == -1 and call(ln=None) == -1 and call(d=None) == -1 and call(c=None) == -1
+    for bad in [dict(B=0), dict(L=0), dict(nmin=0), dict(nmin=3, nmax=2), dict(nmax=17), dict(hits=0),
+                dict(K=0), dict(K=33)]:
+        assert call(**bad) == -2, bad

@@ -1,0 +1,42 @@
+"""GPU parity of the n-gram (prompt-lookup) proposer against oracle.ngram:
+bit-exact drafts and counts."""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import ngram
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(gpu_lib, hist, lens, n_min, n_max, hits, K):
+    import torch
+    d, c = gpu_lib.ngram_propose(torch.from_numpy(np.ascontiguousarray(hist)).cuda(),
+                                 torch.from_numpy(np.ascontiguousarray(lens)).cuda(), n_min, n_max, hits, K)
+    torch.cuda.synchronize()
+    return d.cpu().numpy(), c.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,L,vocab,n_min,n_max,hits,K", [(64, 4096, 32000, 1, 4, 1, 5), (32, 20000, 500, 2, 8, 2, 8),
+                                                          (16, 300, 3, 1, 16, 3, 32), (128, 2048, 50000, 3, 3, 1, 1)],
+                         ids=lambda x: str(x))
+def test_proposals_match_oracle(gpu_lib, B, L, vocab, n_min, n_max, hits, K):
+    hist, lens = workloads.make_histories(B, L, vocab, seed=L + vocab, workers=workloads.default_workers())
+    print(f"[ngram] B={B} L={L} vocab={vocab} n={n_min}..{n_max} hits={hits} K={K}", file=sys.stderr, flush=True)
+    d, c = _run(gpu_lib, hist, lens, n_min, n_max, hits, K)
+    rd, rc = ngram.propose(hist, lens, n_min, n_max, hits, K)
+    np.testing.assert_array_equal(c, rc)
+    np.testing.assert_array_equal(d, rd)
+
+
+def test_edge_lengths(gpu_lib):
+    rng = np.random.default_rng(7)
+    B, L = 40, 64
+    hist = rng.integers(0, 3, (B, L)).astype(np.int32)
+    lens = np.concatenate([np.arange(0, 20), rng.integers(0, L + 1, 18), [L, L + 50]]).astype(np.int32)
+    d, c = _run(gpu_lib, hist, lens, 1, 5, 1, 6)
+    rd, rc = ngram.propose(hist, np.minimum(lens, L), 1, 5, 1, 6)
+    np.testing.assert_array_equal(c, rc)
+    np.testing.assert_array_equal(d, rd)
