@@ -158,6 +158,51 @@ def tree_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def ngram_bench(args):
+    """Prompt-lookup proposals for B histories (every history token read once)."""
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verify_spec_amd as sv
+    import workloads
+    B, L, vocab, n_min, n_max, hits, K = 1024, 16384, 32000, 1, 4, 1, 5
+    log(f"generating {B} histories of up to {L} tokens")
+    hist, lens = workloads.make_histories(B, L, vocab, workers=workloads.default_workers())
+    h, ln = torch.from_numpy(hist).cuda(), torch.from_numpy(lens).cuda()
+    for _ in range(args.warmup):
+        out = sv.ngram_propose(h, ln, n_min, n_max, hits, K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        out = sv.ngram_propose(h, ln, n_min, n_max, hits, K)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    nbytes = int(np.sum(lens)) * 4
+    cnt = out[1].cpu().numpy()
+    line = {"metric": "proposals/s + HBM GB/s (% peak), n-gram prompt lookup", "value": B / step_s,
+            "unit": "proposals/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "int32", "data": "synthetic",
+            "config": {"workload": f"ngram: {B} histories, lengths uniform in [{L // 2}, {L}], vocab {vocab}, "
+                                   f"copies of earlier spans with probability 1/2; n = {n_min}..{n_max}, "
+                                   f"min hits {hits}, K = {K}", "B": B, "L_max": L},
+            "hbm_gbps_algorithmic": nbytes / step_s / 1e9, "hbm_frac_of_peak": nbytes / step_s / 1e9 / PEAK_HBM_GBS,
+            "bytes_per_step": nbytes, "proposal_rate": float(np.mean(cnt > 0)), "mean_draft": float(np.mean(cnt)),
+            "roofline": None, "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        from oracle import ngram
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds or done == 0:
+            b = done % B
+            ngram.propose_sequence(hist[b, : lens[b]], n_min, n_max, hits, K)
+            done += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": done / dt, "unit": "proposals/s", "cores": 1, "kind": "oracle",
+                                "sample": f"{done} histories of the timed batch, numpy, one thread",
+                                "seconds": round(dt, 2)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +214,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--tree", action="store_true",
                     help="greedy token-tree verification: 128 trees of 32 nodes, V=128256 bf16")
+    ap.add_argument("--ngram", action="store_true",
+                    help="prompt-lookup proposer: 1024 histories of up to 16384 tokens, n = 1..4, K = 5")
     ap.add_argument("--ragged", action="store_true",
                     help="per-sequence draft counts K_b uniform on [1, K] (spec_verify_ragged with "
                          "per-position counters); bytes count the rows actually read")
@@ -187,6 +234,9 @@ def main():
     sv.load()
     if args.tree:
         tree_bench(args)
+        return
+    if args.ngram:
+        ngram_bench(args)
         return
     if args.copy_calibration > 0:
         src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
