@@ -21,7 +21,10 @@
 //    fast draw takes rho as 1 and adds |sum P' - sum Q'| to its error bound.
 //  - Streaming.  The row is cut into segments of one or more wave iterations
 //    of 64 lanes x U units (16-byte vectors, or single elements on the scalar
-//    path); wave w takes segments w, w + 16, ...  Each lane sums its weights
+//    path; U = 2 on the vector path: for this pattern, two rows per CU at
+//    scattered addresses, fewer loads in flight per wave measured faster
+//    than U = 4 or 8 or a prefetch of the next iteration); wave w takes
+//    segments w, w + 16, ...  Each lane sums its weights
 //    in fp32 pairwise groups, a DPP wave sum gives the segment's mass (kept in
 //    LDS), and sum P', sum Q' go to fp64 lane totals.
 //  - Select.  Wave 0 scans the segment masses for the segment holding t,
@@ -185,7 +188,7 @@ __device__ inline FastWeight fast_weight(const Params& p, const SeqRec& rec) {
 template <int DT, bool VEC>
 struct Geometry {
   static constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  static constexpr int U = VEC ? 4 : 8;
+  static constexpr int U = VEC ? 2 : 8;
   static constexpr int kIterUnits = kWave * U;
   long units;
   int iters, nseg;
