@@ -319,6 +319,7 @@ def main():
         "hbm_frac_of_peak": (swept + reread) / step_s / 1e9 / PEAK_HBM_GBS,
         "bytes_per_step": {"swept": swept, "decisive_reread": reread},
         "mean_accepted": float(np.mean(n_host)),
+        "fp64_draw_fraction": None if (greedy or args.ragged) else float(np.mean((flags.cpu().numpy() & sv.FLAG_FP64) != 0)),
         "roofline": None,
         "cpu_baseline": None,
     }

@@ -55,7 +55,8 @@ typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype_t;
 #define SPECV_MAX_TREE     64   /* token-tree nodes: one per lane of a wave */
 #define SPECV_MAX_NGRAM    16   /* largest n-gram the prompt-lookup proposer matches */
 
-/* Flag bits of out_flags (bit 0 is unused). */
+/* Flag bits of out_flags. */
+#define SPECV_FLAG_FP64      1  /* the draw was made by the fp64 path: the fp32 draw could not certify its token */
 #define SPECV_FLAG_ZW_ZERO   2  /* residual mass was zero after rounding; drew from p_n instead */
 #define SPECV_FLAG_BAD_DRAFT 4  /* an evaluated draft id was outside [0, V) and was rejected */
 

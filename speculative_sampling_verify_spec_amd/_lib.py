@@ -18,7 +18,7 @@ SPECV_F32, SPECV_BF16 = 0, 1
 SPECV_MAX_K = 32
 SPECV_MAX_TREE = 64
 SPECV_MAX_NGRAM = 16
-FLAG_ZW_ZERO, FLAG_BAD_DRAFT = 2, 4
+FLAG_FP64, FLAG_ZW_ZERO, FLAG_BAD_DRAFT = 1, 2, 4
 
 ERRORS = {0: "SPECV_OK", -1: "SPECV_E_NULL", -2: "SPECV_E_SHAPE", -3: "SPECV_E_DTYPE", -4: "SPECV_E_TEMP",
           -5: "SPECV_E_WORKSPACE", -6: "SPECV_E_ALIGN", -7: "SPECV_E_HIP"}

@@ -463,7 +463,7 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec) {
       certain = fmin(t - lo, hi - t) > fast_bound(SP, SQ, p.V, g.iters, BONUS);
   }
   if (lane == 0) {
-    if (p.out_flags) p.out_flags[s] = rec.flags;
+    if (p.out_flags) p.out_flags[s] = rec.flags | (certain ? 0 : SPECV_FLAG_FP64);
     if (certain) {
       p.out_tokens[s * (p.K + 1) + rec.n] = token;
     } else {

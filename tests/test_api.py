@@ -34,6 +34,7 @@ def test_header_constants_match_binding():
     assert consts["SPECV_MAX_TREE"] == sv.SPECV_MAX_TREE
     assert consts["SPECV_MAX_NGRAM"] == sv.SPECV_MAX_NGRAM
     assert consts["SPECV_FLAG_ZW_ZERO"] == sv.FLAG_ZW_ZERO and consts["SPECV_FLAG_BAD_DRAFT"] == sv.FLAG_BAD_DRAFT
+    assert consts["SPECV_FLAG_FP64"] == sv.FLAG_FP64
     for code, name in sv.ERRORS.items():
         assert consts.get(name, 0) == code, name
 

@@ -1,0 +1,66 @@
+"""Draws placed right next to an interval edge.
+
+The fp32 draw certifies a token only when t = u Z lies further from both ends
+of the token's interval than its error bound, which is of the order of 1e-6
+of the mass.  Uniforms chosen so that t lies between 1e-11 and 1e-7 of the mass
+above the lower end of the oracle's token therefore must all go to the fp64
+draw (SPECV_FLAG_FP64).  The fp64 draw is good to ~1e-12, so it must return the
+oracle's token exactly; no near-tie excuse applies at these margins.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import speculative_sampling_verify_spec_amd as sv
+import workloads
+from gpu_helpers import run_gpu
+from oracle.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+def edge_uniforms(b, ref, lo_min=1e-3, margin_lo=1e-11, margin_hi=1e-7):
+    """Replace u_resample of every sequence whose oracle token interval
+    [lo, hi) allows it by the smallest float32 above lo (kept when its margin
+    u - lo lies in (margin_lo, margin_hi)).  Returns the new uniforms, the
+    chosen sequences and their tokens."""
+    ur = b.u_resample.copy()
+    chosen, tokens = [], []
+    for s in range(b.B):
+        n = int(ref.n_accepted[s])
+        j = int(ref.tokens[s, n])
+        lo, hi = oracle.draw_interval(b.logits_p[s], b.logits_q[s], n, j, 0.5, b.T, b.dtype)
+        if lo < lo_min:
+            continue
+        u = np.float32(lo)
+        if float(u) <= lo:
+            u = np.nextafter(u, np.float32(1.0))
+        margin = float(u) - lo
+        if not (margin_lo < margin < margin_hi) or hi - float(u) < 1e-6:
+            continue
+        ur[s] = u
+        chosen.append(s)
+        tokens.append(j)
+    return ur, np.array(chosen, dtype=np.int64), np.array(tokens, dtype=np.int64)
+
+
+@pytest.mark.parametrize("cfg,nseq", [(1, None), (2, 32), (3, 16)], ids=["small-bf16", "headline-bf16", "sharp-fp32"])
+def test_draws_at_an_edge_go_to_fp64_and_match(gpu_lib, cfg, nseq):
+    seqs = None if nseq is None else range(nseq)
+    b = workloads.make_batch(cfg, seqs=seqs, workers=workloads.default_workers())
+    ref = oracle.verify_batch(b)
+    ur, chosen, tokens = edge_uniforms(b, ref)
+    print(f"cfg {cfg}: {len(chosen)} of {b.B} sequences get an edge uniform", flush=True)
+    assert len(chosen) >= b.B // 4
+    b2 = dataclasses.replace(b, u_resample=ur)
+    g = run_gpu(gpu_lib, b2)
+    ref2 = oracle.verify_batch(b2)
+    # the accept decisions do not change; the oracle keeps its token
+    np.testing.assert_array_equal(ref2.n_accepted, ref.n_accepted)
+    np.testing.assert_array_equal(ref2.tokens[chosen, ref.n_accepted[chosen]], tokens)
+    assert np.all(g.flags[chosen] & sv.FLAG_FP64), "an edge draw was certified by the fp32 path"
+    same = chosen[g.n[chosen] == ref2.n_accepted[chosen]]
+    np.testing.assert_array_equal(g.tokens[same], ref2.tokens[same])
+    compare(b2, g, ref2).check()
