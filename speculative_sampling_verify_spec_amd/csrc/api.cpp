@@ -24,8 +24,9 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
   Layout L{};
   // sweep chunks: equal shares of a row, each at most one workgroup's worth
   const int per_vec = vec ? (dtype == SPECV_BF16 ? 8 : 4) : 1;
-  const int lane_elems = vec ? (dtype == SPECV_BF16 ? kSweepElems<1, true>() : kSweepElems<0, true>())
-                             : kSweepElems<0, false>();
+  const int lane_elems = !vec ? kSweepElems<0, false, false>()
+                         : greedy ? (dtype == SPECV_BF16 ? kSweepElems<1, true, true>() : kSweepElems<0, true, true>())
+                                  : (dtype == SPECV_BF16 ? kSweepElems<1, true, false>() : kSweepElems<0, true, false>());
   L.ch1 = kBlock * lane_elems;  // elements per chunk, at most
   const long units = static_cast<long>(V) / per_vec;
   const long units_per_chunk = static_cast<long>(kBlock) * (lane_elems / per_vec);

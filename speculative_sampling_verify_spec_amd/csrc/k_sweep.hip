@@ -43,11 +43,12 @@ __device__ inline const void* sweep_row(const Params& p, uint32_t row) {
 // end reads the chunk's last unit again (real values of the same chunk, so
 // they leave its maximum unchanged; sums must skip them).  Scalar path:
 // elements past the end read as -inf.  Returns the chunk's unit range.
-template <int DT, bool VEC>
-__device__ inline void load_chunk(const Params& p, const void* r, uint32_t chunk, float (&e)[kSweepElems<DT, VEC>()],
-                                  uint32_t& live, long& lo, long& hi) {
+template <int DT, bool VEC, bool ARGMAX>
+__device__ inline void load_chunk(const Params& p, const void* r, uint32_t chunk,
+                                  float (&e)[kSweepElems<DT, VEC, ARGMAX>()], uint32_t& live, long& lo, long& hi) {
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  constexpr int IT = kSweepElems<DT, VEC>() / PV;
+  constexpr int IT = kSweepElems<DT, VEC, ARGMAX>() / PV;
+  static_assert(IT <= 32, "one live bit per slot");
   lo = static_cast<long>(chunk) * p.cq + min(static_cast<int>(chunk), p.cr);
   hi = lo + p.cq + (static_cast<int>(chunk) < p.cr ? 1 : 0);
   const uint32_t n = static_cast<uint32_t>(hi - lo);  // cq or cq + 1 units
@@ -77,7 +78,7 @@ __device__ inline void load_chunk(const Params& p, const void* r, uint32_t chunk
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
-  constexpr int N = kSweepElems<DT, VEC>();
+  constexpr int N = kSweepElems<DT, VEC, false>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
   const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);
   const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   float e[N];
   uint32_t live;
   long lo, hi;
-  load_chunk<DT, VEC>(p, sweep_row<DT>(p, row), chunk, e, live, lo, hi);
+  load_chunk<DT, VEC, false>(p, sweep_row<DT>(p, row), chunk, e, live, lo, hi);
 
   float m = -INFINITY;
 #pragma unroll
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
-  constexpr int N = kSweepElems<DT, VEC>();
+  constexpr int N = kSweepElems<DT, VEC, true>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
   const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);  // target rows only: s * (K+1) + k
   const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
   float e[N];
   uint32_t live;
   long lo, hi;
-  load_chunk<DT, VEC>(p, row_ptr<DT>(p.lp, row, p.V), chunk, e, live, lo, hi);
+  load_chunk<DT, VEC, true>(p, row_ptr<DT>(p.lp, row, p.V), chunk, e, live, lo, hi);
   // the lane's largest value, then the lowest index holding it (a backward
   // pass of selects over the lane's elements, which it visits in increasing
   // index order); repeated tail units carry their real index

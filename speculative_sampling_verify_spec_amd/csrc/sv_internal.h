@@ -12,11 +12,13 @@ constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kWaves = kBlock / kWave;
 constexpr int kMaxDrawChunks = 256;   // fp64 draw chunks per row: one wave combines them, 4 per lane
 
-// Elements one lane of the row sweep holds: six 16-byte units on the vector
-// path, sixteen single elements on the scalar path.
-template <int DT, bool VEC>
+// Elements one lane of a row sweep holds: 16-byte units on the vector path,
+// 14 for the log-sum-exp sweep and 16 for the arg-max sweep (the fastest of
+// 6 to 18 at the headline shapes: fewer, larger workgroups beat higher
+// occupancy here), sixteen single elements on the scalar path.
+template <int DT, bool VEC, bool ARGMAX>
 constexpr int kSweepElems() {
-  return VEC ? 6 * (DT == 1 ? 8 : 4) : 16;
+  return VEC ? (ARGMAX ? 16 : 14) * (DT == 1 ? 8 : 4) : 16;
 }
 
 // Per-sequence record written by the acceptance scan and read by the fp64 draw.
