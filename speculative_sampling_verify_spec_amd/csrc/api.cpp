@@ -24,16 +24,27 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
   Layout L{};
   // sweep chunks: equal shares of a row, each at most one workgroup's worth
   const int per_vec = vec ? (dtype == SPECV_BF16 ? 8 : 4) : 1;
-  const int lane_elems = !vec ? kSweepElems<0, false, false>()
-                         : greedy ? (dtype == SPECV_BF16 ? kSweepElems<1, true, true>() : kSweepElems<0, true, true>())
-                                  : (dtype == SPECV_BF16 ? kSweepElems<1, true, false>() : kSweepElems<0, true, false>());
-  L.ch1 = kBlock * lane_elems;  // elements per chunk, at most
+  const bool bf = dtype == SPECV_BF16;
+  auto elems = [&](bool large) {
+    if (!vec) return kSweepElems<0, false, false, false>();
+    if (greedy) return large ? (bf ? kSweepElems<1, true, true, true>() : kSweepElems<0, true, true, true>())
+                             : (bf ? kSweepElems<1, true, true, false>() : kSweepElems<0, true, true, false>());
+    return large ? (bf ? kSweepElems<1, true, false, true>() : kSweepElems<0, true, false, true>())
+                 : (bf ? kSweepElems<1, true, false, false>() : kSweepElems<0, true, false, false>());
+  };
+  const long rows = static_cast<long>(B) * (greedy ? K + 1 : 2 * K + 1);
   const long units = static_cast<long>(V) / per_vec;
-  const long units_per_chunk = static_cast<long>(kBlock) * (lane_elems / per_vec);
-  L.nch1 = static_cast<int>((units + units_per_chunk - 1) / units_per_chunk);
+  auto chunks = [&](int lane_elems) {  // at least one, also for a row shorter than one vector
+    const long units_per_chunk = static_cast<long>(kBlock) * (lane_elems / per_vec);
+    return units > 0 ? (units + units_per_chunk - 1) / units_per_chunk : 1L;
+  };
+  // the large shape when it still gives the launch enough workgroups
+  L.sweep_large = vec && rows * chunks(elems(true)) >= kSweepLargeMinGroups ? 1 : 0;
+  const int lane_elems = elems(L.sweep_large != 0);
+  L.ch1 = kBlock * lane_elems;  // elements per chunk, at most
+  L.nch1 = static_cast<int>(chunks(lane_elems));
   L.cq = static_cast<int>(units / L.nch1);
   L.cr = static_cast<int>(units % L.nch1);
-  const long rows = static_cast<long>(B) * (greedy ? K + 1 : 2 * K + 1);
   size_t off = 0;
   L.part = off;
   off = align_up(off + static_cast<size_t>(rows) * L.nch1 * kWaves * sizeof(float2));
@@ -141,6 +152,7 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   P.ch1 = L.ch1;
   P.cq = L.cq;
   P.cr = L.cr;
+  P.sweep_large = L.sweep_large;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = static_cast<hipEvent_t>(ev_sweep_begin), e1 = static_cast<hipEvent_t>(ev_sweep_end);
   const bool timed = e0 && e1;
@@ -262,6 +274,7 @@ int spec_verify_tree_greedy(const void* logits, const int32_t* tree_tokens, cons
   P.ch1 = L.ch1;
   P.cq = L.cq;
   P.cr = L.cr;
+  P.sweep_large = L.sweep_large;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (launch_sweep_argmax(P, dtype, st, nullptr, nullptr) != hipSuccess) return SPECV_E_HIP;
   if (launch_tree_scan(P, st) != hipSuccess) return SPECV_E_HIP;

@@ -43,11 +43,12 @@ __device__ inline const void* sweep_row(const Params& p, uint32_t row) {
 // end reads the chunk's last unit again (real values of the same chunk, so
 // they leave its maximum unchanged; sums must skip them).  Scalar path:
 // elements past the end read as -inf.  Returns the chunk's unit range.
-template <int DT, bool VEC, bool ARGMAX>
+template <int DT, bool VEC, bool ARGMAX, bool LARGE>
 __device__ inline void load_chunk(const Params& p, const void* r, uint32_t chunk,
-                                  float (&e)[kSweepElems<DT, VEC, ARGMAX>()], uint32_t& live, long& lo, long& hi) {
+                                  float (&e)[kSweepElems<DT, VEC, ARGMAX, LARGE>()], uint32_t& live, long& lo,
+                                  long& hi) {
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  constexpr int IT = kSweepElems<DT, VEC, ARGMAX>() / PV;
+  constexpr int IT = kSweepElems<DT, VEC, ARGMAX, LARGE>() / PV;
   static_assert(IT <= 32, "one live bit per slot");
   lo = static_cast<long>(chunk) * p.cq + min(static_cast<int>(chunk), p.cr);
   hi = lo + p.cq + (static_cast<int>(chunk) < p.cr ? 1 : 0);
@@ -76,9 +77,9 @@ __device__ inline void load_chunk(const Params& p, const void* r, uint32_t chunk
   }
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool LARGE>
 __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
-  constexpr int N = kSweepElems<DT, VEC, false>();
+  constexpr int N = kSweepElems<DT, VEC, false, LARGE>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
   const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);
   const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   float e[N];
   uint32_t live;
   long lo, hi;
-  load_chunk<DT, VEC, false>(p, sweep_row<DT>(p, row), chunk, e, live, lo, hi);
+  load_chunk<DT, VEC, false, LARGE>(p, sweep_row<DT>(p, row), chunk, e, live, lo, hi);
 
   float m = -INFINITY;
 #pragma unroll
@@ -124,9 +125,9 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
     p.part[(static_cast<long>(row) * p.nch1 + chunk) * kWaves + threadIdx.x / kWave] = make_float2(M, static_cast<float>(S));
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool LARGE>
 __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
-  constexpr int N = kSweepElems<DT, VEC, true>();
+  constexpr int N = kSweepElems<DT, VEC, true, LARGE>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
   const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);  // target rows only: s * (K+1) + k
   const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
   float e[N];
   uint32_t live;
   long lo, hi;
-  load_chunk<DT, VEC, true>(p, row_ptr<DT>(p.lp, row, p.V), chunk, e, live, lo, hi);
+  load_chunk<DT, VEC, true, LARGE>(p, row_ptr<DT>(p.lp, row, p.V), chunk, e, live, lo, hi);
   // the lane's largest value, then the lowest index holding it (a backward
   // pass of selects over the lane's elements, which it visits in increasing
   // index order); repeated tail units carry their real index
@@ -172,19 +173,25 @@ hipError_t launch_evented(Kern k, const dim3& grid, hipStream_t st, hipEvent_t e
 hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const long rows = static_cast<long>(p.nseq) * (2 * p.K + 1);
   const dim3 grid(static_cast<unsigned>(rows * p.nch1));
-  if (dtype == 1) return p.vec ? launch_evented(k_sweep_lse<1, true>, grid, st, e0, e1, p)
-                               : launch_evented(k_sweep_lse<1, false>, grid, st, e0, e1, p);
-  return p.vec ? launch_evented(k_sweep_lse<0, true>, grid, st, e0, e1, p)
-               : launch_evented(k_sweep_lse<0, false>, grid, st, e0, e1, p);
+  const bool L = p.sweep_large != 0;
+  if (dtype == 1) return !p.vec ? launch_evented(k_sweep_lse<1, false, false>, grid, st, e0, e1, p)
+                         : L ? launch_evented(k_sweep_lse<1, true, true>, grid, st, e0, e1, p)
+                             : launch_evented(k_sweep_lse<1, true, false>, grid, st, e0, e1, p);
+  return !p.vec ? launch_evented(k_sweep_lse<0, false, false>, grid, st, e0, e1, p)
+         : L ? launch_evented(k_sweep_lse<0, true, true>, grid, st, e0, e1, p)
+             : launch_evented(k_sweep_lse<0, true, false>, grid, st, e0, e1, p);
 }
 
 hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const long rows = static_cast<long>(p.nseq) * (p.K + 1);
   const dim3 grid(static_cast<unsigned>(rows * p.nch1));
-  if (dtype == 1) return p.vec ? launch_evented(k_sweep_argmax<1, true>, grid, st, e0, e1, p)
-                               : launch_evented(k_sweep_argmax<1, false>, grid, st, e0, e1, p);
-  return p.vec ? launch_evented(k_sweep_argmax<0, true>, grid, st, e0, e1, p)
-               : launch_evented(k_sweep_argmax<0, false>, grid, st, e0, e1, p);
+  const bool L = p.sweep_large != 0;
+  if (dtype == 1) return !p.vec ? launch_evented(k_sweep_argmax<1, false, false>, grid, st, e0, e1, p)
+                         : L ? launch_evented(k_sweep_argmax<1, true, true>, grid, st, e0, e1, p)
+                             : launch_evented(k_sweep_argmax<1, true, false>, grid, st, e0, e1, p);
+  return !p.vec ? launch_evented(k_sweep_argmax<0, false, false>, grid, st, e0, e1, p)
+         : L ? launch_evented(k_sweep_argmax<0, true, true>, grid, st, e0, e1, p)
+             : launch_evented(k_sweep_argmax<0, true, false>, grid, st, e0, e1, p);
 }
 
 }  // namespace sv

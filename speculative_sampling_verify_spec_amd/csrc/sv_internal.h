@@ -13,13 +13,17 @@ constexpr int kWaves = kBlock / kWave;
 constexpr int kMaxDrawChunks = 256;   // fp64 draw chunks per row: one wave combines them, 4 per lane
 
 // Elements one lane of a row sweep holds: 16-byte units on the vector path,
-// 14 for the log-sum-exp sweep and 16 for the arg-max sweep (the fastest of
-// 6 to 18 at the headline shapes: fewer, larger workgroups beat higher
-// occupancy here), sixteen single elements on the scalar path.
-template <int DT, bool VEC, bool ARGMAX>
+// sixteen single elements on the scalar path.  The vector path has two
+// shapes.  The large one (14 units for the log-sum-exp sweep, 16 for the
+// arg-max sweep: the fastest of 6 to 18 on large launches, where fewer,
+// larger workgroups beat higher occupancy) serves launches of at least
+// kSweepLargeMinGroups workgroups; smaller launches, which the large shape
+// would fill only a few times over, take 6 units.
+template <int DT, bool VEC, bool ARGMAX, bool LARGE>
 constexpr int kSweepElems() {
-  return VEC ? (ARGMAX ? 16 : 14) * (DT == 1 ? 8 : 4) : 16;
+  return VEC ? (LARGE ? (ARGMAX ? 16 : 14) : 6) * (DT == 1 ? 8 : 4) : 16;
 }
+constexpr long kSweepLargeMinGroups = 6144;
 
 // Per-sequence record written by the acceptance scan and read by the fp64 draw.
 struct SeqRec {
@@ -82,6 +86,7 @@ struct Params {
   int32_t* queue;            // [B] their ids (from the first sequence of the launch on)
   int nch1, ch1;             // sweep chunks per row, elements per sweep chunk (at most)
   int cq, cr;                // sweep chunk c spans c*cq + min(c, cr) .. + cq + (c < cr) units
+  int sweep_large;           // the sweep runs its large shape (see kSweepElems)
   int R3, ch3;               // fp64 draw chunks per row, elements per chunk
   int seq0, nseq;            // the sequences a launch covers
 };
@@ -90,6 +95,7 @@ struct Params {
 struct Layout {
   size_t part, rec, xsum, queue, qcount, total;
   int nch1, ch1, cq, cr, R3, ch3;
+  int sweep_large;  // the sweep's large shape (see kSweepElems)
 };
 
 Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy);

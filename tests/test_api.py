@@ -72,6 +72,15 @@ def _call(lib, **kw):
                               a["flags"], None, None)
 
 
+def test_workspace_size_for_rows_shorter_than_a_vector(lib):
+    """Rows shorter than one 16-byte vector: the sizing also lays out the
+    vector path (never used for them) and must not divide by a zero chunk count."""
+    for V in (1, 2, 3, 5, 7):
+        for dt in (F32, BF16):
+            for T in (0.0, 1.0):
+                assert sv.workspace_size(2, 3, V, dt, T) > 0, (V, dt, T)
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=2), -3), (dict(dtype=-1), -3),
     (dict(T=-0.5), -4), (dict(T=float("nan")), -4), (dict(T=float("inf")), -4), (dict(T=1e-45), -4),
