@@ -145,6 +145,19 @@ def test_greedy_small_shapes_with_ties(gpu_lib, shape):
         rep.check()
 
 
+@pytest.mark.parametrize("B,K,V,T", [(192, 8, 65536, 0.0), (192, 4, 65536, 0.9)], ids=["greedy", "sampling"])
+def test_fp32_launches_large_enough_for_the_large_sweep_shape(gpu_lib, B, K, V, T):
+    """fp32 rows in launches of at least 6144 sweep workgroups (the large
+    shape: 16-byte units, 4096 of them per chunk), compared in full."""
+    rows = B * (K + 1 if T == 0.0 else 2 * K + 1)
+    assert rows * -(-(V // 4) // 4096) >= 6144
+    draft = "greedy-mask" if T == 0.0 else "noise"
+    wl = workloads.Workload("fp32-large", B, K, V, "fp32", float(np.float32(T)), 2.0, 1.1, draft, 0.8)
+    b = workloads.make_batch(1, wl=wl, seed=7, workers=workloads.default_workers())
+    say(f"[parity] {wl.describe()}")
+    compare(b, run_gpu(gpu_lib, b), oracle.verify_batch(b)).check()
+
+
 def test_identical_rows_accept_everything(gpu_lib):
     rng = np.random.default_rng(3)
     B, K, V = 16, 6, 3000
