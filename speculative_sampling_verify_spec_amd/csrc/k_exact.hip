@@ -235,7 +235,7 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
     }
     const double inc = wave_inclusive_scan(v);
     const double err_inc = wave_inclusive_scan(err);
-    const double z = __shfl(inc, kWave - 1, kWave);
+    const double z = readlane_f64(inc, kWave - 1);
     const double t = ur * z;
     const uint64_t hit = __ballot(inc > t);
     const uint64_t pos = __ballot(v > 0.0);
@@ -277,9 +277,9 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
       base = run;
       err_before = erun;
     }
-    rc = __shfl(rc, L, kWave);
-    base = __shfl(base, L, kWave);
-    err_before = __shfl(err_before, L, kWave);
+    rc = __builtin_amdgcn_readlane(rc, L);  // L is uniform (from ballots)
+    base = readlane_f64(base, L);
+    err_before = readlane_f64(err_before, L);
     // t may lie before the located chunk when it is within the base's error,
     // and the first-order correction needs rho near 1
     const bool bad_rho = !bonus && !usep && !(fabs(rho - 1.0) <= kKappa);

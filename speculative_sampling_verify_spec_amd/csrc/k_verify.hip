@@ -142,7 +142,7 @@ __device__ inline SeqRec accept_scan(const Params& p, long s) {
     const uint64_t lim = (kb >= 64) ? ~0ull : ((1ull << kb) - 1ull);
     const uint64_t rejected = ~static_cast<uint64_t>(__ballot(accept)) & lim;
     const int n = rejected ? __ffsll(static_cast<unsigned long long>(rejected)) - 1 : kb;
-    const bool bad = __shfl(valid ? 1 : 0, n < kb ? n : 0, kWave) == 0 && n < kb;
+    const bool bad = __builtin_amdgcn_readlane(valid ? 1 : 0, n < kb ? n : 0) == 0 && n < kb;
     if (lane <= K && lane != n) p.out_tokens[s * (K + 1) + lane] = lane < n ? xk : -1;
     if (lane == 0) {
       p.out_n[s] = n;
@@ -379,7 +379,7 @@ __device__ inline bool rescan_segment(const void* rp, const void* rq, const Fast
 #pragma unroll
       for (int k = 0; k < G::PV; ++k) mine += wv[k];
       const double inc = wave_inclusive_scan(mine);
-      const double total = __shfl(inc, kWave - 1, kWave);
+      const double total = readlane_f64(inc, kWave - 1);
       const uint64_t hit = __ballot(base + inc > t);
       if (hit) {
         const int L = __ffsll(static_cast<unsigned long long>(hit)) - 1;
@@ -398,11 +398,11 @@ __device__ inline bool rescan_segment(const void* rp, const void* rq, const Fast
             }
           }
         }
-        tk = __shfl(tk, L, kWave);
+        tk = __builtin_amdgcn_readlane(tk, L);
         if (tk < 0) return false;  // the lane's sum crossed t only by rounding
         *token = static_cast<int>((ubase + i * kWave + L) * G::PV + tk);
-        *lo = __shfl(tlo, L, kWave);
-        *hi = __shfl(thi, L, kWave);
+        *lo = readlane_f64(tlo, L);
+        *hi = readlane_f64(thi, L);
         return true;
       }
       base += total;
@@ -436,7 +436,7 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec) {
     if (j < g.nseg) mine += segA[j];
   }
   const double inc = wave_inclusive_scan(mine);
-  const double Z = __shfl(inc, kWave - 1, kWave);
+  const double Z = readlane_f64(inc, kWave - 1);
   const double t = static_cast<double>(p.ur[s]) * Z;
   const uint64_t hit = __ballot(inc > t);
   bool certain = false;
@@ -456,8 +456,8 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec) {
       }
       jbase = run;
     }
-    jseg = __shfl(jseg, L, kWave);
-    jbase = __shfl(jbase, L, kWave);
+    jseg = __builtin_amdgcn_readlane(jseg, L);  // L is uniform (from a ballot)
+    jbase = readlane_f64(jbase, L);
     double lo = 0.0, hi = 0.0;
     if (jseg >= 0 && rescan_segment<DT, VEC, BONUS>(rp, rq, wt, g, jseg, jbase, t, &token, &lo, &hi))
       certain = fmin(t - lo, hi - t) > fast_bound(SP, SQ, p.V, g.iters, BONUS);

@@ -95,10 +95,44 @@ __device__ inline double exp_f64(double y, const ExpConsts& e) {
 }
 
 // ----------------------------------------------------------- reductions --
+// Cross-lane steps by DPP (data-parallel primitives: a VALU operand read from
+// another lane of the same row of 16, or broadcast between rows), which take
+// a few cycles where an LDS permute takes tens.  Lanes outside the row/bank
+// masks, and sources outside the row, give 0.  All 64 lanes must be active.
+template <int CTRL, int ROW_MASK, int BANK_MASK = 0xf>
+__device__ inline int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, true);
+}
+template <int CTRL, int ROW_MASK, int BANK_MASK = 0xf>
+__device__ inline double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp_i32<CTRL, ROW_MASK, BANK_MASK>(static_cast<int>(b));
+  const int hi = dpp_i32<CTRL, ROW_MASK, BANK_MASK>(static_cast<int>(b >> 32));
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+__device__ inline double readlane_f64(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+// Wave reductions: butterflies within each row of 16 lanes (quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror), then
+// row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2 and 3, so lane
+// 63 holds the result, which every lane gets as a scalar.  Fixed order, so
+// deterministic.
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, __int_as_float(dpp_i32<0xb1, 0xf>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i32<0x4e, 0xf>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i32<0x141, 0xf>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_i32<0x140, 0xf>(__float_as_int(v))));
+  // rows outside the broadcast masks take 0 from the DPP; max with the value itself keeps them
+  const float b15 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xa, 0xf, false));
+  v = fmaxf(v, b15);
+  const float b31 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xc, 0xf, false));
+  v = fmaxf(v, b31);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ inline int wave_min_i32(int v) {
@@ -114,9 +148,13 @@ __device__ inline int wave_max_i32(int v) {
 }
 
 __device__ inline double wave_sum(double v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f64<0xb1, 0xf>(v);
+  v += dpp_f64<0x4e, 0xf>(v);
+  v += dpp_f64<0x141, 0xf>(v);
+  v += dpp_f64<0x140, 0xf>(v);
+  v += dpp_f64<0x142, 0xa>(v);
+  v += dpp_f64<0x143, 0xc>(v);
+  return readlane_f64(v, 63);
 }
 
 // fp32 sum over a whole wave (all 64 lanes active) by DPP: butterflies within
@@ -200,13 +238,18 @@ __device__ inline float block_max(float v, float* lds /* >= kWaves */) {
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ inline double wave_inclusive_scan(double v) {
-  const int lane = threadIdx.x % kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double u = __shfl_up(v, o, kWave);
-    if (lane >= o) v += u;
-  }
-  return v;
+  // within each row of 16: the sum of the last four lanes (row_shr 1..3 of
+  // the inputs), then + the value 4 lanes back (lanes 4..15), then + the
+  // value 8 lanes back (lanes 8..15); then the rows' totals by broadcast
+  double s = v;
+  s += dpp_f64<0x111, 0xf>(v);
+  s += dpp_f64<0x112, 0xf>(v);
+  s += dpp_f64<0x113, 0xf>(v);
+  s += dpp_f64<0x114, 0xf, 0xe>(s);
+  s += dpp_f64<0x118, 0xf, 0xc>(s);
+  s += dpp_f64<0x142, 0xa>(s);  // rows 1 and 3: + lane 15 of the row before
+  s += dpp_f64<0x143, 0xc>(s);  // rows 2 and 3: + lane 31
+  return s;
 }
 
 // Exclusive prefix sum of one double per thread over a workgroup of NW
