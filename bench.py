@@ -42,7 +42,16 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published peak
 HEADLINE = 2
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "sweep_lse_headline_counters.md")
-SWEEP_SOURCE = os.path.join(ROOT, "speculative_sampling_verify_spec_amd", "csrc", "k_sweep.hip")
+# the sweep kernel's source: its file and the headers it includes (hashed in this order)
+SWEEP_SOURCES = [os.path.join(ROOT, "speculative_sampling_verify_spec_amd", "csrc", f)
+                 for f in ("k_sweep.hip", "sv_device.h", "sv_internal.h")]
+
+
+def sweep_source_sha256() -> str:
+    h = hashlib.sha256()
+    for f in SWEEP_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -80,7 +89,7 @@ def counter_traffic(swept_bytes: int):
     if not os.path.exists(COUNTER_SUMMARY):
         return None
     text = open(COUNTER_SUMMARY).read()
-    src = hashlib.sha256(open(SWEEP_SOURCE, "rb").read()).hexdigest()
+    src = sweep_source_sha256()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.e+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != src:

@@ -39,8 +39,8 @@ __global__ __launch_bounds__(kBlock) void k_greedy_scan(Params p) {
   const uint64_t lim = (1ull << kb) - 1ull;
   const uint64_t miss = ~static_cast<uint64_t>(__ballot(match)) & lim;
   const int n = miss ? __ffsll(static_cast<unsigned long long>(miss)) - 1 : kb;
-  const int an = __shfl(a, n, kWave);
-  const bool bad = n < kb && __shfl(valid ? 1 : 0, n, kWave) == 0;
+  const int an = __builtin_amdgcn_readlane(a, n);  // n is uniform (from a ballot)
+  const bool bad = n < kb && __builtin_amdgcn_readlane(valid ? 1 : 0, n) == 0;
   if (lane <= K) p.out_tokens[s * (K + 1) + lane] = lane < n ? xk : (lane == n ? an : -1);
   if (lane == 0) {
     p.out_n[s] = n;

@@ -73,11 +73,10 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree_scan(Params p) {
   const uint64_t ok = static_cast<uint64_t>(__ballot(edge_ok || v >= N));
   const bool accepted = v < N && (set & ~ok) == 0;
   // deepest accepted node, lowest index among equals (the root always qualifies)
-  int key = accepted ? (depth << 8) | (kWave - 1 - v) : -1;
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, kWave));
-  const int d = kWave - 1 - (key & 0xff), dd = key >> 8;
-  const uint64_t path = __shfl(set, d, kWave);
+  const int key = wave_max_i32(accepted ? (depth << 8) | (kWave - 1 - v) : -1);
+  const int d = kWave - 1 - (key & 0xff), dd = key >> 8;  // uniform
+  const uint64_t path = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(set >> 32), d))) << 32) |
+                        static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(set), d));
   int32_t* ot = p.out_tokens + s * N;
   int32_t* op = p.out_path ? p.out_path + s * N : nullptr;
   if (v < N && ((path >> v) & 1ull)) {  // a node of the path: its token and index at its depth

@@ -135,16 +135,30 @@ __device__ inline float wave_max(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// One step of an order-independent reduction: lanes outside the row mask
+// see their own value, which leaves them unchanged.
+template <int CTRL, int ROW_MASK>
+__device__ inline int dpp_keep(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+template <typename Op>
+__device__ inline int wave_reduce_i32(int v, Op op) {
+  v = op(v, dpp_keep<0xb1, 0xf>(v));
+  v = op(v, dpp_keep<0x4e, 0xf>(v));
+  v = op(v, dpp_keep<0x141, 0xf>(v));
+  v = op(v, dpp_keep<0x140, 0xf>(v));
+  v = op(v, dpp_keep<0x142, 0xa>(v));
+  v = op(v, dpp_keep<0x143, 0xc>(v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 __device__ inline int wave_min_i32(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce_i32(v, [](int a, int b) { return min(a, b); });
 }
 
 __device__ inline int wave_max_i32(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce_i32(v, [](int a, int b) { return max(a, b); });
 }
 
 __device__ inline double wave_sum(double v) {
@@ -175,36 +189,29 @@ __device__ inline float wave_sum_f32(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Combine (max, sum-scaled-to-max) pairs where sum = sum 2^((x - max) c).
-__device__ inline void lse_merge(float& m, float& s, float m2, float s2, float c) {
-  const float M = fmaxf(m, m2);
-  const float a = (m == -INFINITY) ? 0.f : s * ex2((m - M) * c);
-  const float b = (m2 == -INFINITY) ? 0.f : s2 * ex2((m2 - M) * c);
-  m = M;
-  s = a + b;
-}
-
-__device__ inline void wave_lse(float& m, float& s, float c) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, kWave);
-    const float s2 = __shfl_xor(s, o, kWave);
-    lse_merge(m, s, m2, s2, c);
-  }
-}
-
 // (value, index) arg-max merge: larger value wins, equal values keep the lower index.
 __device__ inline void argmax_merge(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
 
+template <int CTRL, int ROW_MASK>
+__device__ inline void argmax_step(float& v, int& i) {
+  const float v2 = __int_as_float(dpp_keep<CTRL, ROW_MASK>(__float_as_int(v)));
+  const int i2 = dpp_keep<CTRL, ROW_MASK>(i);
+  argmax_merge(v, i, v2, i2);
+}
+
+// Every lane gets the wave's (largest value, lowest index holding it); the
+// merge is a total order, so the DPP order gives the same answer as any other.
 __device__ inline void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(v, o, kWave);
-    const int i2 = __shfl_xor(i, o, kWave);
-    argmax_merge(v, i, v2, i2);
-  }
+  argmax_step<0xb1, 0xf>(v, i);
+  argmax_step<0x4e, 0xf>(v, i);
+  argmax_step<0x141, 0xf>(v, i);
+  argmax_step<0x140, 0xf>(v, i);
+  argmax_step<0x142, 0xa>(v, i);
+  argmax_step<0x143, 0xc>(v, i);
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
 }
 
 // Workgroup-wide sum of one double per thread over NW waves; every thread
