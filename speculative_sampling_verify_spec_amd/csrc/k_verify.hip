@@ -24,9 +24,9 @@
 //    path; U = 2 on the vector path: for this pattern, two rows per CU at
 //    scattered addresses, fewer loads in flight per wave measured faster
 //    than U = 4 or 8 or a prefetch of the next iteration); wave w takes
-//    segments w, w + 16, ...  Each lane sums its weights
-//    in fp32 pairwise groups, a DPP wave sum gives the segment's mass (kept in
-//    LDS), and sum P', sum Q' go to fp64 lane totals.
+//    segments w, w + 16, ...  Each lane sums its weights in fp32 pairwise
+//    groups, a DPP wave sum gives the segment's mass (kept in LDS), and
+//    sum P', sum Q' go to fp64 lane totals.
 //  - Select.  Wave 0 scans the segment masses for the segment holding t,
 //    recomputes that segment's weights and finds the token with wave scans in
 //    token order.  The answer stands when t is further from both ends of the
