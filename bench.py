@@ -40,6 +40,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published peak
+LLC_BYTES = 256 << 20            # MI355X last-level (Infinity) cache
+
+
+def input_copies(nbytes: int) -> int:
+    """Device copies of a step's input to rotate through: enough that at least
+    twice the last-level cache is read between two uses of one copy, so no
+    step is served from what the previous use of its input left there."""
+    return max(2, -(-2 * LLC_BYTES // max(nbytes, 1)) + 1)
 HEADLINE = 2
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "sweep_lse_headline_counters.md")
 # the sweep kernel's source: its file and the headers it includes (hashed in this order)
@@ -131,16 +139,18 @@ def tree_bench(args):
     log(f"generating {B} trees of {N} nodes, V={V} bf16")
     tb = workloads.make_tree_batch(B, N, V, "bf16", workers=workloads.default_workers())
     lg = torch.from_numpy(tb.logits.view(np.int16)).cuda().view(torch.bfloat16)
+    ncopy = input_copies(lg.numel() * 2)
+    lgs = [lg] + [lg.clone() for _ in range(ncopy - 1)]  # used in turn
     tok_in = torch.from_numpy(tb.tokens).cuda()
     par = torch.from_numpy(tb.parents).cuda()
     ws = torch.empty(int(sv.load().spec_verify_tree_workspace_size(B, N, V, sv.SPECV_BF16)), dtype=torch.uint8,
                      device="cuda")
-    for _ in range(args.warmup):
-        out = sv.verify_tree_greedy(lg, tok_in, par, workspace=ws)
+    for i in range(args.warmup):
+        out = sv.verify_tree_greedy(lgs[i % ncopy], tok_in, par, workspace=ws)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        out = sv.verify_tree_greedy(lg, tok_in, par, workspace=ws)
+    for i in range(args.steps):
+        out = sv.verify_tree_greedy(lgs[i % ncopy], tok_in, par, workspace=ws)
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
     n = out[2].cpu().numpy()
@@ -152,7 +162,8 @@ def tree_bench(args):
             "config": {"workload": f"tree-bf16: {B} trees of {N} nodes (chains branching with probability 1/2), "
                                    f"V={V} bf16, greedy", "B": B, "N": N, "V": V},
             "hbm_gbps_algorithmic": nbytes / step_s / 1e9, "hbm_frac_of_peak": nbytes / step_s / 1e9 / PEAK_HBM_GBS,
-            "bytes_per_step": nbytes, "mean_accepted": float(np.mean(n)), "roofline": None, "cpu_baseline": None}
+            "bytes_per_step": nbytes, "mean_accepted": float(np.mean(n)), "input_copies": ncopy, "roofline": None,
+            "cpu_baseline": None}
     if not args.no_cpu_baseline:
         from oracle import tree
         done, t0 = 0, time.perf_counter()
@@ -178,12 +189,14 @@ def ngram_bench(args):
     log(f"generating {B} histories of up to {L} tokens")
     hist, lens = workloads.make_histories(B, L, vocab, workers=workloads.default_workers())
     h, ln = torch.from_numpy(hist).cuda(), torch.from_numpy(lens).cuda()
-    for _ in range(args.warmup):
-        out = sv.ngram_propose(h, ln, n_min, n_max, hits, K)
+    ncopy = input_copies(h.numel() * 4)
+    hs = [h] + [h.clone() for _ in range(ncopy - 1)]  # used in turn
+    for i in range(args.warmup):
+        out = sv.ngram_propose(hs[i % ncopy], ln, n_min, n_max, hits, K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        out = sv.ngram_propose(h, ln, n_min, n_max, hits, K)
+    for i in range(args.steps):
+        out = sv.ngram_propose(hs[i % ncopy], ln, n_min, n_max, hits, K)
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
     nbytes = int(np.sum(lens)) * 4
@@ -197,6 +210,7 @@ def ngram_bench(args):
                                    f"min hits {hits}, K = {K}", "B": B, "L_max": L},
             "hbm_gbps_algorithmic": nbytes / step_s / 1e9, "hbm_frac_of_peak": nbytes / step_s / 1e9 / PEAK_HBM_GBS,
             "bytes_per_step": nbytes, "proposal_rate": float(np.mean(cnt > 0)), "mean_draft": float(np.mean(cnt)),
+            "input_copies": ncopy,
             "roofline": None, "cpu_baseline": None}
     if not args.no_cpu_baseline:
         from oracle import ngram
@@ -277,11 +291,19 @@ def main():
     kb = torch.from_numpy(kb_host).cuda() if args.ragged else None
     stats = torch.zeros(2 * K, dtype=torch.int64, device="cuda")
 
+    # the logits in several device copies, used in turn (the draft tokens and
+    # uniforms, a few KB, are shared)
+    ncopy = input_copies(lp.numel() * lp.element_size() + (0 if lq is None else lq.numel() * lq.element_size()))
+    copies = [(lp, lq)] + [(lp.clone(), None if lq is None else lq.clone()) for _ in range(ncopy - 1)]
+    turn = [0]
+
     def step(e=None):
+        cp, cq = copies[turn[0] % ncopy]
+        turn[0] += 1
         if args.ragged:
-            rc = sv.spec_verify_ragged(lp, lq, x, kb, ua, ur, T, tokens, n_acc, ws, position_stats=stats)
+            rc = sv.spec_verify_ragged(cp, cq, x, kb, ua, ur, T, tokens, n_acc, ws, position_stats=stats)
         else:
-            rc = sv.spec_verify(lp, lq, x, ua, ur, T, tokens, n_acc, ws, out_flags=flags, events=e, extended=True)
+            rc = sv.spec_verify(cp, cq, x, ua, ur, T, tokens, n_acc, ws, out_flags=flags, events=e, extended=True)
         if rc != 0:
             raise RuntimeError(sv.strerror(rc))
 
@@ -328,6 +350,7 @@ def main():
         "hbm_frac_of_peak": (swept + reread) / step_s / 1e9 / PEAK_HBM_GBS,
         "bytes_per_step": {"swept": swept, "decisive_reread": reread},
         "mean_accepted": float(np.mean(n_host)),
+        "input_copies": ncopy,
         "fp64_draw_fraction": None if (greedy or args.ragged) else float(np.mean((flags.cpu().numpy() & sv.FLAG_FP64) != 0)),
         "roofline": None,
         "cpu_baseline": None,
