@@ -58,12 +58,10 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
   if (need > ch) ch = (need + 1023) / 1024 * 1024;
   L.ch3 = static_cast<int>(ch);
   L.R3 = static_cast<int>((V + ch - 1) / ch);
-  L.rec = off;
-  off = align_up(off + static_cast<size_t>(B) * sizeof(SeqRec));
   L.xsum = off;
   off = align_up(off + static_cast<size_t>(B) * L.R3 * 5 * sizeof(double));
   L.queue = off;
-  off = align_up(off + static_cast<size_t>(B) * sizeof(int32_t));
+  off = align_up(off + static_cast<size_t>(B) * sizeof(SeqRec));
   L.qcount = off;
   off = align_up(off + sizeof(uint32_t));
   L.total = off;
@@ -170,9 +168,8 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   P.c = static_cast<float>(c64);
   P.inv_t = 1.0 / T64;
   P.ec = make_exp_consts();
-  P.rec = reinterpret_cast<SeqRec*>(ws + L.rec);
   P.xsum = reinterpret_cast<double*>(ws + L.xsum);
-  P.queue = reinterpret_cast<int32_t*>(ws + L.queue);
+  P.queue = reinterpret_cast<SeqRec*>(ws + L.queue);
   P.qcount = reinterpret_cast<uint32_t*>(ws + L.qcount);
   P.R3 = L.R3;
   P.ch3 = L.ch3;

@@ -6,7 +6,8 @@
 // P(v) = exp(x/T - L'p), Q(v) = exp(y/T - L'q) normalised by their own sums:
 // w = max(0, P - rho Q) / sum P with rho = sum P / sum Q.
 //
-// Two kernels walk the queue the fast draw filled:
+// Two kernels walk the queue the fast draw filled (each entry is the
+// sequence's whole record, read together with the queue's length):
 //   exact_chunks (queued sequences x chunks of ch3 >= 1024 tokens): per chunk
 //        sum P, sum Q, A = sum max(0, P - Q), G = sum_{P > Q} Q and
 //        H = sum_{near flip} Q, the Q-mass within a relative kKappa of P = Q.
@@ -377,13 +378,25 @@ __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const
 }
 
 // ---------------------------------------------------------------- kernels --
+// Queue entry `slot`, read before the queue's length is known so that both
+// loads are in flight together: the index is clamped into the queue's storage
+// (branch-free), and the entry is used only when slot < count.  The loops
+// test `first.seq >= 0` (true for every live entry) with a non-short-circuit &
+// in their condition, which keeps the compiler from moving this load behind
+// the test of the count.
+__device__ inline SeqRec entry_ahead(const Params& p, long slot) {
+  return p.queue[p.seq0 + min(slot, static_cast<long>(p.nseq) - 1)];
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kXBlock) void k_exact_chunks(Params p) {
+  const SeqRec first = entry_ahead(p, blockIdx.x / p.R3);
   const long count = static_cast<long>(p.qcount[0]);
-  for (long item = blockIdx.x; item < count * p.R3; item += gridDim.x) {
-    const long s = p.queue[p.seq0 + item / p.R3];
+  for (long item = blockIdx.x; (item < count * p.R3) & (first.seq >= 0); item += gridDim.x) {
+    SeqRec rec = first;
+    if (item != blockIdx.x) rec = p.queue[p.seq0 + item / p.R3];
+    const long s = rec.seq;
     const int r = static_cast<int>(item % p.R3);
-    const SeqRec rec = p.rec[s];
     const bool bonus = rec.n == rec.kb;
     exact_chunk_sums<DT, VEC>(p, decisive_rows<DT>(p, s, rec), exact_weight(p, rec), bonus, r,
                               p.xsum + (s * p.R3 + r) * 5);
@@ -392,10 +405,12 @@ __global__ __launch_bounds__(kXBlock) void k_exact_chunks(Params p) {
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kXBlock) void k_exact_select(Params p) {
+  const SeqRec first = entry_ahead(p, blockIdx.x);
   const long count = static_cast<long>(p.qcount[0]);
-  for (long e = blockIdx.x; e < count; e += gridDim.x) {
-    const long s = p.queue[p.seq0 + e];
-    const SeqRec rec = p.rec[s];
+  for (long e = blockIdx.x; (e < count) & (first.seq >= 0); e += gridDim.x) {
+    SeqRec rec = first;
+    if (e != blockIdx.x) rec = p.queue[p.seq0 + e];
+    const long s = rec.seq;
     const bool bonus = rec.n == rec.kb;
     __syncthreads();  // shared scalars of the previous entry are no longer read
     int token;

@@ -150,10 +150,9 @@ __device__ inline SeqRec accept_scan(const Params& p, long s) {
       r.n = n;
       r.kb = kb;
       r.flags = bad ? SPECV_FLAG_BAD_DRAFT : 0;
-      r.pad = 0;
+      r.seq = static_cast<int32_t>(s);
       r.lzp = sL[n];
       r.lzq = n < kb ? sL[K + 1 + n] : 0.0;
-      p.rec[s] = r;  // read by the fp64 draw if this sequence is queued
       sRec = r;
     }
   }
@@ -468,7 +467,7 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec) {
       p.out_tokens[s * (p.K + 1) + rec.n] = token;
     } else {
       const uint32_t slot = atomicAdd(&p.qcount[0], 1u);
-      p.queue[p.seq0 + slot] = static_cast<int32_t>(s);
+      p.queue[p.seq0 + slot] = rec;
     }
   }
 }

@@ -25,12 +25,14 @@ constexpr int kSweepElems() {
 }
 constexpr long kSweepLargeMinGroups = 6144;
 
-// Per-sequence record written by the acceptance scan and read by the fp64 draw.
+// Per-sequence record of the acceptance scan; the fast draw puts it, with the
+// sequence's index, in the fp64 draw's queue, so that one 32-byte load gives
+// that draw everything it needs.
 struct SeqRec {
   int32_t n;       // accepted draft tokens
   int32_t kb;      // the sequence's draft count (n == kb: bonus draw)
   int32_t flags;   // SPECV_FLAG_* set so far
-  int32_t pad;
+  int32_t seq;     // the sequence (in a queue entry)
   double lzp, lzq; // log2 sum_v 2^(x_v c) of the decisive target / draft row (fp32-accurate)
 };
 static_assert(sizeof(SeqRec) == 32, "SeqRec layout");
@@ -80,10 +82,9 @@ struct Params {
   int32_t* out_flags;        // [B] or null
   // workspace
   float2* part;              // [rows][nch1][kWaves] (R, s) sweep partials, or (max, index bits) in greedy mode
-  SeqRec* rec;               // [B]
   double* xsum;              // [B][R3][5] exact draw chunk sums (queued sequences)
   uint32_t* qcount;          // [1] sequences queued for the exact draw
-  int32_t* queue;            // [B] their ids (from the first sequence of the launch on)
+  SeqRec* queue;             // [B] their records (from the first sequence of the launch on)
   int nch1, ch1;             // sweep chunks per row, elements per sweep chunk (at most)
   int cq, cr;                // sweep chunk c spans c*cq + min(c, cr) .. + cq + (c < cr) units
   int sweep_large;           // the sweep runs its large shape (see kSweepElems)
@@ -93,7 +94,7 @@ struct Params {
 
 // Workspace layout (byte offsets), shared by spec_verify_workspace_size and the launcher.
 struct Layout {
-  size_t part, rec, xsum, queue, qcount, total;
+  size_t part, xsum, queue, qcount, total;
   int nch1, ch1, cq, cr, R3, ch3;
   int sweep_large;  // the sweep's large shape (see kSweepElems)
 };
