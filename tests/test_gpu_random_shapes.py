@@ -1,0 +1,49 @@
+"""Many small random workloads against the oracle.
+
+Each case draws its shape (B, K, V), logit dtype, temperature (greedy a quarter
+of the time), logit recipe and, for about a third of the cases, per-sequence
+draft counts from its own seeded generator; the HIP path must meet the parity
+rule of oracle.parity on every one.  Small vocabularies (1, 2, 7 tokens) and
+sizes that are and are not whole 16-byte vectors are among the choices.
+"""
+import dataclasses
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_helpers import run_gpu
+from oracle.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = int(os.environ.get("SPECV_RANDOM_CASES", "64"))  # more on demand
+VOCABS = [1, 2, 7, 8, 63, 64, 257, 1000, 4096, 5003, 20000]
+
+
+def random_batch(case: int):
+    rng = np.random.default_rng(5000 + case)
+    B = int(rng.integers(1, 40))
+    K = int(rng.integers(1, 13))
+    V = int(rng.choice(VOCABS))
+    dt = str(rng.choice(["fp32", "bf16"]))
+    greedy = bool(rng.random() < 0.25)
+    T = 0.0 if greedy else float(np.float32(rng.choice([0.3, 0.7, 1.0, 1.7])))
+    wl = workloads.Workload(f"random-{case}", B, K, V, dt, T, float(rng.choice([0.5, 2.0, 4.0])),
+                            float(rng.choice([0.0, 1.1, 3.3])), "greedy-mask" if greedy else "noise",
+                            float(rng.choice([0.1, 0.8, 2.0])))
+    b = workloads.make_batch(1, wl=wl, seed=case)
+    if rng.random() < 0.3:
+        b = dataclasses.replace(b, num_drafts=workloads.ragged_draft_counts(B, K, seed=case, low=0))
+    return b
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_workload_matches_oracle(gpu_lib, case):
+    b = random_batch(case)
+    ragged = getattr(b, "num_drafts", None) is not None
+    print(f"[random] case {case}: {b.wl.describe()}{' ragged' if ragged else ''}", file=sys.stderr, flush=True)
+    compare(b, run_gpu(gpu_lib, b), oracle.verify_batch(b)).check()
