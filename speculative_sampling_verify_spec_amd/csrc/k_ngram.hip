@@ -7,11 +7,13 @@
 // (1 <= e <= L - 1, so a token follows it) where h[e-n..e) == h[L-n..L).
 // Ends are visited in rounds of 4096, sixteen per thread; a round's tokens and
 // the 16 before them are staged in LDS by coalesced loads (the next round's
-// loads issued before this round's work).  An end's match length m(e) is the
-// run of equal tokens in NM independent comparisons with the suffix (no
-// branches), and it is counted, for every size n <= m(e), in per-thread
-// registers (count and latest end per size, compiled for the largest size in
-// use); waves reduce them and LDS atomics gather one value per wave.
+// loads issued before this round's work).  Each thread first compares the
+// last token of its ends with the suffix's (one compare per end, a bit mask);
+// size 1 is counted from the mask, and only the ends that passed go on to the
+// remaining comparisons, whose run of matches m(e) is counted for every size
+// n <= m(e) in per-thread registers (count and latest end per size, compiled
+// for the largest size in use); waves reduce them and LDS atomics gather one
+// value per wave.
 // Thread 0 takes the largest n in [n_min, n_max] seen at least min_hits
 // times, and the workgroup writes h[e*..min(e* + K, L)) for its latest end
 // e*, then -1 up to K.  Without such an n the proposal is empty.
@@ -79,20 +81,34 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
     for (int r = 0; r < kNgPer; ++r) win[NM + r * kNgBlock + threadIdx.x] = v[r];
     if (threadIdx.x < NM) win[threadIdx.x] = hv;
     __syncthreads();
+    // first tokens: bit r of `first` says whether end r's last token equals
+    // the suffix's (m(e) >= 1: e < L, and the suffix has a token); that token,
+    // h[e - 1], is the thread's own v[r]
+    uint32_t first = 0;
 #pragma unroll
     for (int r = 0; r < kNgPer; ++r) {
       const int e = base + r * kNgBlock + threadIdx.x;
-      const int k = e - 1 - w0;  // win index of h[e - 1]
-      // match length m(e): trailing ones of the NM independent comparisons,
+      first |= ((e < L && jmax > 0 && v[r] == sf[0]) ? 1u : 0u) << r;
+    }
+    // size 1 straight from the bits (ends increase with r)
+    c[0] += __popc(first);
+    if (first) l[0] = base + (31 - __clz(first)) * kNgBlock + threadIdx.x;
+    // longer sizes: only the ends whose last token matched, in increasing order
+    uint32_t more = NM > 1 ? first : 0u;
+    while (more) {
+      const int r = __builtin_ctz(more);
+      more &= more - 1u;
+      const int e = base + r * kNgBlock + threadIdx.x;
+      const int k = e - 1 - w0;
+      // match length m(e): trailing ones of the NM comparisons (j = 0 matched),
       // cut to the sizes that exist (j < jmax and h[e-1-j] inside the history)
-      uint32_t bits = 0;
+      uint32_t bits = 1u;
 #pragma unroll
-      for (int j = 0; j < NM; ++j) bits |= (win[k - j] == sf[j] ? 1u : 0u) << j;
-      const int lim = e < L ? min(jmax, e) : 0;
-      bits &= (1u << lim) - 1u;
+      for (int j = 1; j < NM; ++j) bits |= (win[k - j] == sf[j] ? 1u : 0u) << j;
+      bits &= (1u << min(jmax, e)) - 1u;
       const int m = __builtin_ctz(~bits);
 #pragma unroll
-      for (int n = 0; n < NM; ++n) {
+      for (int n = 1; n < NM; ++n) {
         c[n] += m > n ? 1 : 0;
         l[n] = m > n ? e : l[n];
       }
