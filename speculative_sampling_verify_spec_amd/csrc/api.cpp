@@ -64,8 +64,33 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
   off = align_up(off + static_cast<size_t>(B) * sizeof(SeqRec));
   L.qcount = off;
   off = align_up(off + sizeof(uint32_t));
+  // the split fast draw (batches of at most kSplitMaxSeqs): segment masses,
+  // per-workgroup sums and per-sequence counters
+  const long nsplit = B <= kSplitMaxSeqs ? B : 0;
+  const SegGeom sg = seg_geom(V, per_vec, vec);
+  L.segm = off;
+  off = align_up(off + static_cast<size_t>(nsplit) * sg.nseg * sizeof(float));
+  L.spq = off;
+  off = align_up(off + static_cast<size_t>(nsplit) * kMaxSplit * 2 * sizeof(double));
+  L.vcount = off;
+  off = align_up(off + static_cast<size_t>(nsplit) * sizeof(uint32_t));
   L.total = off;
   return L;
+}
+
+// Workgroups per sequence for the fast draw: one per idle CU, at most one per
+// block of kVerifyWaves segments and at most kMaxSplit; 1 for larger batches
+// (or if the device cannot be queried).
+int verify_split(int B, int V, int dtype, bool vec) {
+  if (B > kSplitMaxSeqs) return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 1;
+  const int per_vec = vec ? (dtype == SPECV_BF16 ? 8 : 4) : 1;
+  const SegGeom sg = seg_geom(V, per_vec, vec);
+  const int blocks = (sg.nseg + kVerifyWaves - 1) / kVerifyWaves;
+  return std::max(1, std::min(std::min(cus / B, blocks), kMaxSplit));
 }
 
 namespace {
@@ -173,6 +198,11 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   P.qcount = reinterpret_cast<uint32_t*>(ws + L.qcount);
   P.R3 = L.R3;
   P.ch3 = L.ch3;
+  P.split = verify_split(B, V, dtype, vec);
+  P.nseg = seg_geom(V, vec ? (dtype == SPECV_BF16 ? 8 : 4) : 1, vec).nseg;
+  P.segm = reinterpret_cast<float*>(ws + L.segm);
+  P.spq = reinterpret_cast<double*>(ws + L.spq);
+  P.vcount = reinterpret_cast<uint32_t*>(ws + L.vcount);
 
   if (launch_sweep_lse(P, dtype, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess) return SPECV_E_HIP;
   if (launch_verify(P, dtype, st) != hipSuccess) return SPECV_E_HIP;

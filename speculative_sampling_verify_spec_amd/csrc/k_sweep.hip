@@ -84,7 +84,15 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);
   const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
   const uint32_t row = static_cast<uint32_t>(p.seq0) * (2u * p.K + 1u) + local;
-  if (blockIdx.x == 0 && threadIdx.x == 0) p.qcount[0] = 0u;  // the fp64 draw's queue, filled after this kernel
+  if (blockIdx.x == 0) {  // state the kernels after this one fill
+    if (threadIdx.x == 0) p.qcount[0] = 0u;  // the fp64 draw's queue
+    if (p.split > 1) {  // the split fast draw: counts to zero, published values to NaN ("not yet")
+      for (int i = threadIdx.x; i < p.nseq; i += kBlock) p.vcount[p.seq0 + i] = 0u;
+      const long nsegs = static_cast<long>(p.nseq) * p.nseg, nsums = static_cast<long>(p.nseq) * kMaxSplit * 2;
+      for (long i = threadIdx.x; i < nsegs; i += kBlock) p.segm[static_cast<long>(p.seq0) * p.nseg + i] = NAN;
+      for (long i = threadIdx.x; i < nsums; i += kBlock) p.spq[static_cast<long>(p.seq0) * kMaxSplit * 2 + i] = NAN;
+    }
+  }
   if (p.kb) {  // per-sequence draft counts: rows past a sequence's own are not read
     const uint32_t per_seq = 2u * p.K + 1u, s = row / per_seq, j = row - s * per_seq;
     const int kb = seq_kb(p, s);

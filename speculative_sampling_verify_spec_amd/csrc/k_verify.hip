@@ -1,6 +1,8 @@
 // The verify step after the row sweep, sampling mode: one workgroup of 1024
 // threads per sequence runs the acceptance scan and then the fast
 // replacement / bonus draw, so no partial result has to cross workgroups.
+// When the batch is small enough to leave CUs idle, a sequence gets `split`
+// workgroups instead (see Split below).
 //
 // Acceptance.  The 16 waves fold the sweep's per-wave (R, s) partials of the
 // sequence's 2K+1 rows into log2 normalisers (fp64 sums with exact
@@ -27,6 +29,16 @@
 //    segments w, w + 16, ...  Each lane sums its weights in fp32 pairwise
 //    groups, a DPP wave sum gives the segment's mass (kept in LDS), and
 //    sum P', sum Q' go to fp64 lane totals.
+//  - Split.  Every workgroup of a split sequence runs the acceptance scan
+//    (cheap, and the same for all) and streams every split-th block of 16
+//    segments.  Each publishes its segment masses and sums in the workspace
+//    (device-scope stores, waited for) and counts itself done on the
+//    sequence's counter; the one that completes the count reads them all and
+//    makes the draw below.  Segment masses are the same values as unsplit.
+//    Device-wide fences (an L2 write-back and invalidate each) measured
+//    slower than the split's gain; instead the sweep leaves NaN in every
+//    published slot, and a NaN read back sends the sequence to the fp64 draw,
+//    so the result never depends on when the stores become visible.
 //  - Select.  Wave 0 scans the segment masses for the segment holding t,
 //    recomputes that segment's weights and finds the token with wave scans in
 //    token order.  The answer stands when t is further from both ends of the
@@ -40,11 +52,10 @@ namespace sv {
 
 namespace {
 
-constexpr int kVBlock = 1024;                 // threads per workgroup
-constexpr int kVWaves = kVBlock / kWave;      // 16
+constexpr int kVBlock = kVerifyBlock;         // threads per workgroup
+constexpr int kVWaves = kVerifyWaves;         // 16
 constexpr int kRowsMax = 2 * SPECV_MAX_K + 1;
 constexpr int kRowsPerWave = (kRowsMax + kVWaves - 1) / kVWaves;  // 5 rows per wave at most
-constexpr int kMaxSegs = 1024;                // segment masses kept in LDS
 
 // ------------------------------------------------------------ acceptance --
 // Fold one lane's (R, s) sweep partial into its running pair (ml, sl):
@@ -71,10 +82,12 @@ __device__ inline double wave_log2z(float ml, double sl) {
   return static_cast<double>(M) + e + __builtin_amdgcn_logf(static_cast<float>(m));
 }
 
-// Runs on the whole workgroup.  Writes the accepted prefix and the padding of
-// out_tokens (slot n is the draw's), out_n, out_logz, and returns the record.
+// Runs on the whole workgroup.  When `writer`, writes the accepted prefix and
+// the padding of out_tokens (slot n is the draw's), out_n and out_logz (the
+// other workgroups of a split sequence compute the same record and write
+// nothing).  Returns the record.
 template <int DT>
-__device__ inline SeqRec accept_scan(const Params& p, long s) {
+__device__ inline SeqRec accept_scan(const Params& p, long s, bool writer) {
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int K = p.K, nrows = 2 * K + 1, np = p.nch1 * kWaves;  // kWaves: the sweep's waves per chunk
   const int kb = seq_kb(p, s);  // the sequence's own draft count
@@ -126,7 +139,7 @@ __device__ inline SeqRec accept_scan(const Params& p, long s) {
     const double lz2 = wave_log2z(ml[r], sl[r]);
     if (lane == 0) {
       sL[i] = lz2;
-      if (p.out_logz) p.out_logz[s * nrows + i] = static_cast<float>(lz2 * M_LN2);
+      if (p.out_logz && writer) p.out_logz[s * nrows + i] = static_cast<float>(lz2 * M_LN2);
     }
   }
   __syncthreads();
@@ -143,9 +156,9 @@ __device__ inline SeqRec accept_scan(const Params& p, long s) {
     const uint64_t rejected = ~static_cast<uint64_t>(__ballot(accept)) & lim;
     const int n = rejected ? __ffsll(static_cast<unsigned long long>(rejected)) - 1 : kb;
     const bool bad = __builtin_amdgcn_readlane(valid ? 1 : 0, n < kb ? n : 0) == 0 && n < kb;
-    if (lane <= K && lane != n) p.out_tokens[s * (K + 1) + lane] = lane < n ? xk : -1;
+    if (writer && lane <= K && lane != n) p.out_tokens[s * (K + 1) + lane] = lane < n ? xk : -1;
     if (lane == 0) {
-      p.out_n[s] = n;
+      if (writer) p.out_n[s] = n;
       SeqRec r;
       r.n = n;
       r.kb = kb;
@@ -187,15 +200,15 @@ __device__ inline FastWeight fast_weight(const Params& p, const SeqRec& rec) {
 template <int DT, bool VEC>
 struct Geometry {
   static constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  static constexpr int U = VEC ? 2 : 8;
+  static constexpr int U = draw_lane_units(VEC);
   static constexpr int kIterUnits = kWave * U;
   long units;
   int iters, nseg;
   __device__ explicit Geometry(int V) {
-    units = VEC ? V / PV : V;  // VEC: V is a multiple of PV
-    const long total = (units + kIterUnits - 1) / kIterUnits;
-    iters = static_cast<int>((total + kMaxSegs - 1) / kMaxSegs);
-    nseg = static_cast<int>((total + iters - 1) / iters);
+    const SegGeom sg = seg_geom(V, PV, VEC);
+    units = sg.units;
+    iters = sg.iters;
+    nseg = sg.nseg;
   }
 };
 
@@ -259,12 +272,15 @@ struct Iter {
 // Stream the decisive row(s): segment masses into segA, fp64 lane totals of
 // P' and Q'.  Per unit the sums are pairwise in fp32, then pairwise over the
 // lane's U units; the residual mass of a lane is sum P' - sum min(P', Q').
+// Segments come in blocks of kVWaves (one per wave); workgroup `part` of a
+// sequence split over `split` takes blocks part, part + split, ...  A
+// segment's mass does not depend on which workgroup computes it.
 template <int DT, bool VEC, bool BONUS>
 __device__ inline void stream_row(const void* rp, const void* rq, const FastWeight& wt, const Geometry<DT, VEC>& g,
-                                  float* segA, double& tsp, double& tsq) {
+                                  int part, int split, float* segA, double& tsp, double& tsq) {
   using G = Geometry<DT, VEC>;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-  for (int j = w; j < g.nseg; j += kVWaves) {
+  for (int j = part * kVWaves + w; j < g.nseg; j += kVWaves * split) {
     float a = 0.f;
     for (int it = 0; it < g.iters; ++it) {
       const long base = (static_cast<long>(j) * g.iters + it) * G::kIterUnits;
@@ -410,8 +426,10 @@ __device__ inline bool rescan_segment(const void* rp, const void* rq, const Fast
   return false;
 }
 
-template <int DT, bool VEC, bool BONUS>
-__device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec) {
+// SPLIT: the sequence's stream is shared by p.split workgroups (`part` is
+// this one's index), which exchange their results through the workspace.
+template <int DT, bool VEC, bool BONUS, bool SPLIT>
+__device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec, int part) {
   using G = Geometry<DT, VEC>;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const G g(p.V);
@@ -421,18 +439,74 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec) {
   __shared__ float segA[kMaxSegs];
   __shared__ double lds[kVWaves];
 
+  const int split = SPLIT ? p.split : 1;
   double tsp = 0.0, tsq = 0.0;
-  stream_row<DT, VEC, BONUS>(rp, rq, wt, g, segA, tsp, tsq);
-  const double SP = block_sum_n<kVWaves>(tsp, lds);  // its barriers also publish segA
-  const double SQ = BONUS ? 0.0 : block_sum_n<kVWaves>(tsq, lds);
+  stream_row<DT, VEC, BONUS>(rp, rq, wt, g, part, split, segA, tsp, tsq);
+  double SP = block_sum_n<kVWaves>(tsp, lds);  // its barriers also publish segA
+  double SQ = BONUS ? 0.0 : block_sum_n<kVWaves>(tsq, lds);
   if (w != 0) return;
 
   // segments per lane, consecutive; wave scan of the lanes' masses
+  constexpr int kPer = kMaxSegs / kWave;
   const int per = (g.nseg + kWave - 1) / kWave;
+  float segv[SPLIT ? kPer : 1];  // split: this lane's segment masses, read from the workspace
   double mine = 0.0;
-  for (int k = 0; k < per; ++k) {
-    const int j = lane * per + k;
-    if (j < g.nseg) mine += segA[j];
+  if constexpr (SPLIT) {
+    // publish this workgroup's segment masses and sums with device-scope
+    // stores over the NaN the sweep left there, wait for them, and count this
+    // workgroup done; the sequence's last workgroup makes the draw
+    float* gseg = p.segm + s * g.nseg;
+    double* gsum = p.spq + (s * kMaxSplit) * 2;
+    for (int k = lane;; k += kWave) {  // this workgroup's k-th segment, in increasing order
+      const int j = ((k / kVWaves) * split + part) * kVWaves + k % kVWaves;
+      if (j >= g.nseg) break;
+      __hip_atomic_store(gseg + j, segA[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (lane == 0) {
+      __hip_atomic_store(gsum + 2 * part, SP, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gsum + 2 * part + 1, SQ, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the stores have completed
+    uint32_t prior = 0;
+    if (lane == 0) prior = __hip_atomic_fetch_add(&p.vcount[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prior = __builtin_amdgcn_readlane(prior, 0);
+    if (prior != static_cast<uint32_t>(split - 1)) return;  // uniform over the wave
+    // the last one: every workgroup's masses and sums (device-scope loads).
+    // A value still NaN is one whose store this workgroup cannot see yet;
+    // rather than wait, the sequence then goes to the fp64 draw, which needs
+    // none of them.  So the draw never depends on the order in which the
+    // other workgroups' stores become visible.
+    bool seen = true;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = lane * per + k;
+      segv[k] = (k < per && j < g.nseg) ? __hip_atomic_load(gseg + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                        : 0.f;
+      seen &= !isnan(segv[k]);
+    }
+    double psp = 0.0, psq = 0.0;
+    if (lane < split) {
+      psp = __hip_atomic_load(gsum + 2 * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      psq = __hip_atomic_load(gsum + 2 * lane + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      seen &= !(isnan(psp) || isnan(psq));
+    }
+    if (__ballot(!seen)) {  // uniform
+      if (lane == 0) {
+        if (p.out_flags) p.out_flags[s] = rec.flags | SPECV_FLAG_FP64;
+        const uint32_t slot = atomicAdd(&p.qcount[0], 1u);
+        p.queue[p.seq0 + slot] = rec;
+      }
+      return;
+    }
+    SP = wave_sum(psp);
+    SQ = BONUS ? 0.0 : wave_sum(psq);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) mine += segv[k];  // adding the zeros past `per` changes nothing
+  } else {
+    for (int k = 0; k < per; ++k) {
+      const int j = lane * per + k;
+      if (j < g.nseg) mine += segA[j];
+    }
   }
   const double inc = wave_inclusive_scan(mine);
   const double Z = readlane_f64(inc, kWave - 1);
@@ -446,11 +520,22 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec) {
     double jbase = 0.0;
     if (lane == L) {
       double run = inc - mine;
-      for (int k = 0; k < per && jseg < 0; ++k) {
-        const int j = lane * per + k;
-        if (j < g.nseg) {
-          if (run + segA[j] > t) jseg = j;
-          else run += segA[j];
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          const int j = lane * per + k;
+          if (jseg < 0 && k < per && j < g.nseg) {
+            if (run + segv[k] > t) jseg = j;
+            else run += segv[k];
+          }
+        }
+      } else {
+        for (int k = 0; k < per && jseg < 0; ++k) {
+          const int j = lane * per + k;
+          if (j < g.nseg) {
+            if (run + segA[j] > t) jseg = j;
+            else run += segA[j];
+          }
         }
       }
       jbase = run;
@@ -472,24 +557,41 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec) {
   }
 }
 
-template <int DT, bool VEC>
+// Workgroup g takes sequence seq0 + g (SPLIT: seq0 + g / split, part g % split).
+template <int DT, bool VEC, bool SPLIT>
 __global__ __launch_bounds__(kVBlock) void k_verify(Params p) {
-  const long s = p.seq0 + blockIdx.x;
-  const SeqRec rec = accept_scan<DT>(p, s);
-  if (rec.n == rec.kb) fast_draw<DT, VEC, true>(p, s, rec);
-  else fast_draw<DT, VEC, false>(p, s, rec);
+  long s = p.seq0 + blockIdx.x;
+  int part = 0;
+  if constexpr (SPLIT) {
+    const uint32_t split = static_cast<uint32_t>(p.split);
+    const uint32_t local = blockIdx.x / split;
+    part = static_cast<int>(blockIdx.x - local * split);
+    s = p.seq0 + local;
+  }
+  const SeqRec rec = accept_scan<DT>(p, s, part == 0);
+  if (rec.n == rec.kb) fast_draw<DT, VEC, true, SPLIT>(p, s, rec, part);
+  else fast_draw<DT, VEC, false, SPLIT>(p, s, rec, part);
+}
+
+template <int DT, bool VEC>
+void launch_verify_t(const Params& p, hipStream_t st) {
+  const dim3 block(kVBlock);
+  const unsigned n = static_cast<unsigned>(p.nseq);
+  if (p.split > 1)
+    hipLaunchKernelGGL((k_verify<DT, VEC, true>), dim3(n * static_cast<unsigned>(p.split)), block, 0, st, p);
+  else
+    hipLaunchKernelGGL((k_verify<DT, VEC, false>), dim3(n), block, 0, st, p);
 }
 
 }  // namespace
 
 hipError_t launch_verify(const Params& p, int dtype, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(p.nseq)), block(kVBlock);
   if (dtype == 1) {
-    if (p.vec) hipLaunchKernelGGL((k_verify<1, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((k_verify<1, false>), grid, block, 0, st, p);
+    if (p.vec) launch_verify_t<1, true>(p, st);
+    else launch_verify_t<1, false>(p, st);
   } else {
-    if (p.vec) hipLaunchKernelGGL((k_verify<0, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((k_verify<0, false>), grid, block, 0, st, p);
+    if (p.vec) launch_verify_t<0, true>(p, st);
+    else launch_verify_t<0, false>(p, st);
   }
   return hipGetLastError();
 }

@@ -25,6 +25,39 @@ constexpr int kSweepElems() {
 }
 constexpr long kSweepLargeMinGroups = 6144;
 
+// The fast draw (k_verify) streams a sequence's decisive row(s) in wave
+// iterations of 64 lanes x kDrawLaneUnits units (16-byte vectors, or single
+// elements on the scalar path), grouped into at most kMaxSegs segments of
+// whole iterations.  Host and kernel share this geometry: the host sizes the
+// split workspace and picks the split from it.
+constexpr int kVerifyBlock = 1024;            // threads per k_verify workgroup
+constexpr int kVerifyWaves = kVerifyBlock / kWave;
+constexpr int kMaxSegs = 1024;                // segments per row, at most
+__host__ __device__ constexpr int draw_lane_units(bool vec) { return vec ? 2 : 8; }
+
+struct SegGeom {
+  long units;  // units of the row (vectors on the vector path, else elements)
+  int iters;   // wave iterations per segment
+  int nseg;    // segments
+};
+
+__host__ __device__ inline SegGeom seg_geom(int V, int per_vec, bool vec) {
+  SegGeom g;
+  g.units = vec ? V / per_vec : V;  // vector path: V is a multiple of per_vec
+  const long iter_units = static_cast<long>(kWave) * draw_lane_units(vec);
+  const long total = g.units > 0 ? (g.units + iter_units - 1) / iter_units : 1;  // at least one iteration
+  g.iters = static_cast<int>((total + kMaxSegs - 1) / kMaxSegs);
+  g.nseg = static_cast<int>((total + g.iters - 1) / g.iters);
+  return g;
+}
+
+// When the batch leaves CUs idle, each sequence's fast draw is split over up
+// to kMaxSplit workgroups (one CU each), which stream interleaved blocks of
+// kVerifyWaves segments; the last of them to finish draws.  Only batches of
+// at most kSplitMaxSeqs sequences are split.
+constexpr int kMaxSplit = 16;
+constexpr int kSplitMaxSeqs = 128;
+
 // Per-sequence record of the acceptance scan; the fast draw puts it, with the
 // sequence's index, in the fp64 draw's queue, so that one 32-byte load gives
 // that draw everything it needs.
@@ -90,11 +123,16 @@ struct Params {
   int sweep_large;           // the sweep runs its large shape (see kSweepElems)
   int R3, ch3;               // fp64 draw chunks per row, elements per chunk
   int seq0, nseq;            // the sequences a launch covers
+  int split;                 // workgroups per sequence in k_verify (1: no split)
+  int nseg;                  // segments of the fast draw's row stream (seg_geom)
+  float* segm;               // split: [B][nseg] segment masses of the fast draw (NaN until published)
+  double* spq;               // split: [B][kMaxSplit][2] sum P', sum Q' of each workgroup (NaN until published)
+  uint32_t* vcount;          // split: [B] workgroups of the sequence done streaming
 };
 
 // Workspace layout (byte offsets), shared by spec_verify_workspace_size and the launcher.
 struct Layout {
-  size_t part, xsum, queue, qcount, total;
+  size_t part, xsum, queue, qcount, segm, spq, vcount, total;
   int nch1, ch1, cq, cr, R3, ch3;
   int sweep_large;  // the sweep's large shape (see kSweepElems)
 };
