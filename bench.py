@@ -232,6 +232,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=HEADLINE, choices=range(5))
+    ap.add_argument("--seqs", type=int, default=0, metavar="N",
+                    help="verify only the first N sequences of the workload (a smaller batch of the same shape)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
@@ -270,9 +272,13 @@ def main():
         log(f"copy calibration: 3 device copies of {args.copy_calibration} bytes")
         del src, dst
     wl = workloads.WORKLOADS[args.workload]
-    log(f"generating {wl.name}: {wl.describe()}")
+    if args.seqs < 0 or args.seqs > wl.B:
+        print(f"--seqs must lie in [1, {wl.B}] for workload {args.workload}", file=sys.stderr)
+        sys.exit(2)
+    seqs = range(args.seqs) if args.seqs else None
+    log(f"generating {wl.name}: {wl.describe()}" + (f", first {args.seqs} sequences" if args.seqs else ""))
     t0 = time.perf_counter()
-    batch = workloads.make_batch(args.workload, workers=workloads.default_workers())
+    batch = workloads.make_batch(args.workload, seqs=seqs, workers=workloads.default_workers())
     log(f"generated in {time.perf_counter() - t0:.1f}s; copying to HBM")
     lp, lq, x, ua, ur = workloads.to_device(batch)
     B, K, V, T = batch.B, batch.K, batch.V, batch.T
@@ -335,7 +341,7 @@ def main():
     reread = 0 if greedy else int(np.sum(np.where(n_host < kbs, 2, 1))) * V * elt
     step_s = wall / args.steps
     line = {
-        "metric": "verified seq-steps/s + HBM GB/s (% peak), B=256 K=8 V=128256 bf16",
+        "metric": f"verified seq-steps/s + HBM GB/s (% peak), B={B} K={K} V={V} {batch.dtype}",
         "value": B / step_s,
         "unit": "verified seq-steps/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -343,7 +349,8 @@ def main():
         "ms_per_step_with_events": None if wall_ev is None else wall_ev / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{wl.name}: verify {wl.describe()}, logits {batch.dtype}"
+        "config": {"workload": f"{wl.name}: verify {batch.wl.describe()}, logits {batch.dtype}"
+                               + (f" (the first {B} sequences of the {wl.B})" if args.seqs else "")
                                + (", per-sequence draft counts uniform on [1, K]" if args.ragged else ""),
                    "B": B, "K": K, "V": V, "logits": batch.dtype, "T": T, "parallelism": "none (one GPU)"},
         "hbm_gbps_algorithmic": (swept + reread) / step_s / 1e9,

@@ -79,8 +79,9 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
 }
 
 // Workgroups per sequence for the fast draw: one per idle CU, at most one per
-// block of kVerifyWaves segments and at most kMaxSplit; 1 for larger batches
-// (or if the device cannot be queried).
+// block of kVerifyWaves segments and at most kMaxSplit; 1 for larger batches,
+// for rows of fewer than kSplitMinBlocks blocks, or if the device cannot be
+// queried.
 int verify_split(int B, int V, int dtype, bool vec) {
   if (B > kSplitMaxSeqs) return 1;
   int dev = 0, cus = 0;
@@ -90,6 +91,7 @@ int verify_split(int B, int V, int dtype, bool vec) {
   const int per_vec = vec ? (dtype == SPECV_BF16 ? 8 : 4) : 1;
   const SegGeom sg = seg_geom(V, per_vec, vec);
   const int blocks = (sg.nseg + kVerifyWaves - 1) / kVerifyWaves;
+  if (blocks < kSplitMinBlocks) return 1;
   return std::max(1, std::min(std::min(cus / B, blocks), kMaxSplit));
 }
 

@@ -57,6 +57,10 @@ __host__ __device__ inline SegGeom seg_geom(int V, int per_vec, bool vec) {
 // at most kSplitMaxSeqs sequences are split.
 constexpr int kMaxSplit = 16;
 constexpr int kSplitMaxSeqs = 128;
+// Rows of fewer blocks are not split: the exchange through the workspace
+// costs about what streaming two blocks in one workgroup instead of two
+// saves (measured at V = 32000).
+constexpr int kSplitMinBlocks = 3;
 
 // Per-sequence record of the acceptance scan; the fast draw puts it, with the
 // sequence's index, in the fp64 draw's queue, so that one 32-byte load gives
