@@ -78,6 +78,8 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
   return L;
 }
 
+namespace {
+
 // Workgroups per sequence for the fast draw: one per idle CU, at most one per
 // block of kVerifyWaves segments and at most kMaxSplit; 1 for larger batches,
 // for rows of fewer than kSplitMinBlocks blocks, or if the device cannot be
@@ -94,8 +96,6 @@ int verify_split(int B, int V, int dtype, bool vec) {
   if (blocks < kSplitMinBlocks) return 1;
   return std::max(1, std::min(std::min(cus / B, blocks), kMaxSplit));
 }
-
-namespace {
 
 bool valid_temperature(float T) {
   if (!std::isfinite(T) || T < 0.f) return false;

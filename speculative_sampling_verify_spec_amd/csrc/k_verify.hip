@@ -35,8 +35,8 @@
 //    (device-scope stores, waited for) and counts itself done on the
 //    sequence's counter; the one that completes the count reads them all and
 //    makes the draw below.  Segment masses are the same values as unsplit.
-//    Device-wide fences (an L2 write-back and invalidate each) measured
-//    slower than the split's gain; instead the sweep leaves NaN in every
+//    Device-wide fences (an L2 write-back and an invalidate) measured about
+//    as costly as the split's gain; instead the sweep leaves NaN in every
 //    published slot, and a NaN read back sends the sequence to the fp64 draw,
 //    so the result never depends on when the stores become visible.
 //  - Select.  Wave 0 scans the segment masses for the segment holding t,
