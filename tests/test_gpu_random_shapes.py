@@ -4,7 +4,9 @@ Each case draws its shape (B, K, V), logit dtype, temperature (greedy a quarter
 of the time), logit recipe and, for about a third of the cases, per-sequence
 draft counts from its own seeded generator; the HIP path must meet the parity
 rule of oracle.parity on every one.  Small vocabularies (1, 2, 7 tokens) and
-sizes that are and are not whole 16-byte vectors are among the choices.
+sizes that are and are not whole 16-byte vectors are among the choices.  A
+second set draws large vocabularies with small batches, which take the split
+fast draw.
 """
 import dataclasses
 import os
@@ -46,4 +48,35 @@ def test_random_workload_matches_oracle(gpu_lib, case):
     b = random_batch(case)
     ragged = getattr(b, "num_drafts", None) is not None
     print(f"[random] case {case}: {b.wl.describe()}{' ragged' if ragged else ''}", file=sys.stderr, flush=True)
+    compare(b, run_gpu(gpu_lib, b), oracle.verify_batch(b)).check()
+
+
+# Large vocabularies with small batches: the fast draw is split over several
+# workgroups per sequence (rows of at least 3 blocks of 16 segments), on the
+# vector and (odd V with bf16) the scalar path.
+N_SPLIT_CASES = int(os.environ.get("SPECV_RANDOM_SPLIT_CASES", "32"))
+SPLIT_VOCABS = [49152, 50257, 65536, 100003, 128256, 152064]
+
+
+def random_split_batch(case: int):
+    rng = np.random.default_rng(9000 + case)
+    B = int(rng.integers(1, 25))
+    K = int(rng.integers(1, 9))
+    V = int(rng.choice(SPLIT_VOCABS))
+    dt = str(rng.choice(["fp32", "bf16"]))
+    T = float(np.float32(rng.choice([0.5, 0.7, 1.0, 1.3])))
+    wl = workloads.Workload(f"random-split-{case}", B, K, V, dt, T, float(rng.choice([1.0, 2.0])),
+                            float(rng.choice([0.0, 1.1])), "noise", float(rng.choice([0.3, 0.7, 1.5])))
+    b = workloads.make_batch(1, wl=wl, seed=case, workers=workloads.default_workers())
+    if rng.random() < 0.3:
+        b = dataclasses.replace(b, num_drafts=workloads.ragged_draft_counts(B, K, seed=case, low=0))
+    return b
+
+
+@pytest.mark.parametrize("case", range(N_SPLIT_CASES))
+def test_random_split_workload_matches_oracle(gpu_lib, case):
+    b = random_split_batch(case)
+    ragged = getattr(b, "num_drafts", None) is not None
+    print(f"[random-split] case {case}: {b.wl.describe()}{' ragged' if ragged else ''}", file=sys.stderr,
+          flush=True)
     compare(b, run_gpu(gpu_lib, b), oracle.verify_batch(b)).check()
