@@ -182,28 +182,41 @@ __device__ inline void load_run(const void* row, long v0, long chi, float (&e)[k
 }
 
 // ---------------------------------------------------------------- select --
-// The draw for one queued sequence from its chunk sums (whole workgroup).
-// Thread 0 gets the token and whether the zero-mass fallback was used.
+// A queued sequence's chunk sums as wave 0 holds them: lane l owns chunks
+// l*per .. l*per + per - 1 (per <= kMaxPer), 0 past the row.  They live at
+// the sequence's queue slot (not its index), so the select can load them
+// together with the queue entry instead of after it.
+struct ChunkSums {
+  double v[kMaxPer][5];
+};
+
+__device__ inline ChunkSums load_chunk_sums(const Params& p, long slot) {
+  ChunkSums cv;
+  const double* base = p.xsum + (p.seq0 + slot) * p.R3 * 5;
+  const int lane = threadIdx.x % kWave, per = (p.R3 + kWave - 1) / kWave;
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) {
+    const int c = lane * per + k;
+    const bool in = threadIdx.x < kWave && k < per && c < p.R3;
+#pragma unroll
+    for (int f = 0; f < 5; ++f) cv.v[k][f] = in ? base[c * 5 + f] : 0.0;
+  }
+  return cv;
+}
+
+// The draw for one queued sequence from its chunk sums (whole workgroup;
+// cv matters in wave 0 only).  Thread 0 gets the token and whether the
+// zero-mass fallback was used.
 template <int DT, bool VEC>
 __device__ inline void select_exact(const Params& p, const Rows<DT>& rows, const ExactWeight& wt, bool bonus,
-                                    const double* cs_base, double ur, int* token, bool* zw_zero) {
+                                    const ChunkSums& cv, double ur, int* token, bool* zw_zero) {
   const int lane = threadIdx.x % kWave;
   __shared__ double s_rho, s_t;
   __shared__ double s_base;
   __shared__ int s_chunk, s_usep, s_exact_total;
   if (threadIdx.x < kWave) {
-    // lane l owns chunks l*per .. l*per + per - 1 (per <= kMaxPer); their
-    // sums are loaded together up front
     const int per = (p.R3 + kWave - 1) / kWave;
-    double cv[kMaxPer][5];
-#pragma unroll
-    for (int k = 0; k < kMaxPer; ++k) {
-      const int c = lane * per + k;
-      const bool in = k < per && c < p.R3;
-#pragma unroll
-      for (int f = 0; f < 5; ++f) cv[k][f] = in ? cs_base[c * 5 + f] : 0.0;
-    }
-    auto cs = [&](int k, int f) { return cv[k][f]; };
+    auto cs = [&](int k, int f) { return cv.v[k][f]; };
     double sp_l = 0.0, sq_l = 0.0;
 #pragma unroll
     for (int k = 0; k < kMaxPer; ++k) {
@@ -399,7 +412,7 @@ __global__ __launch_bounds__(kXBlock) void k_exact_chunks(Params p) {
     const int r = static_cast<int>(item % p.R3);
     const bool bonus = rec.n == rec.kb;
     exact_chunk_sums<DT, VEC>(p, decisive_rows<DT>(p, s, rec), exact_weight(p, rec), bonus, r,
-                              p.xsum + (s * p.R3 + r) * 5);
+                              p.xsum + ((p.seq0 + item / p.R3) * p.R3 + r) * 5);  // by queue slot
   }
 }
 
@@ -407,15 +420,21 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(kXBlock) void k_exact_select(Params p) {
   const SeqRec first = entry_ahead(p, blockIdx.x);
   const long count = static_cast<long>(p.qcount[0]);
+  // the first entry's chunk sums, loaded with the entry (slot clamped like it)
+  const ChunkSums first_cv = load_chunk_sums(p, min(static_cast<long>(blockIdx.x), static_cast<long>(p.nseq) - 1));
   for (long e = blockIdx.x; (e < count) & (first.seq >= 0); e += gridDim.x) {
     SeqRec rec = first;
-    if (e != blockIdx.x) rec = p.queue[p.seq0 + e];
+    ChunkSums cv = first_cv;
+    if (e != blockIdx.x) {
+      rec = p.queue[p.seq0 + e];
+      cv = load_chunk_sums(p, e);
+    }
     const long s = rec.seq;
     const bool bonus = rec.n == rec.kb;
     __syncthreads();  // shared scalars of the previous entry are no longer read
     int token;
     bool zw_zero;
-    select_exact<DT, VEC>(p, decisive_rows<DT>(p, s, rec), exact_weight(p, rec), bonus, p.xsum + s * p.R3 * 5,
+    select_exact<DT, VEC>(p, decisive_rows<DT>(p, s, rec), exact_weight(p, rec), bonus, cv,
                           static_cast<double>(p.ur[s]), &token, &zw_zero);
     if (threadIdx.x == 0) {
       p.out_tokens[s * (p.K + 1) + rec.n] = token;
