@@ -77,23 +77,20 @@ __device__ inline void load_chunk(const Params& p, const void* r, uint32_t chunk
   }
 }
 
-template <int DT, bool VEC, bool LARGE>
+// RAGGED: per-sequence draft counts (a separate instantiation, so that the
+// common case carries no code for them ahead of its loads).
+template <int DT, bool VEC, bool LARGE, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   constexpr int N = kSweepElems<DT, VEC, false, LARGE>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
   const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);
   const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
   const uint32_t row = static_cast<uint32_t>(p.seq0) * (2u * p.K + 1u) + local;
-  if (blockIdx.x == 0) {  // state the kernels after this one fill
-    if (threadIdx.x == 0) p.qcount[0] = 0u;  // the fp64 draw's queue
-    if (p.split > 1) {  // the split fast draw: counts to zero, published values to NaN ("not yet")
-      for (int i = threadIdx.x; i < p.nseq; i += kBlock) p.vcount[p.seq0 + i] = 0u;
-      const long nsegs = static_cast<long>(p.nseq) * p.nseg, nsums = static_cast<long>(p.nseq) * kMaxSplit * 2;
-      for (long i = threadIdx.x; i < nsegs; i += kBlock) p.segm[static_cast<long>(p.seq0) * p.nseg + i] = NAN;
-      for (long i = threadIdx.x; i < nsums; i += kBlock) p.spq[static_cast<long>(p.seq0) * kMaxSplit * 2 + i] = NAN;
-    }
-  }
-  if (p.kb) {  // per-sequence draft counts: rows past a sequence's own are not read
+  // Per-sequence draft counts: rows past a sequence's own are not read.  The
+  // test comes before any store of this kernel, so the compiler may read the
+  // count with a scalar load, which later workgroups find in the scalar cache.
+  // (Block 0 holds a sequence's target row 0, which is always read.)
+  if constexpr (RAGGED) {
     const uint32_t per_seq = 2u * p.K + 1u, s = row / per_seq, j = row - s * per_seq;
     const int kb = seq_kb(p, s);
     if (j <= static_cast<uint32_t>(p.K) ? j > static_cast<uint32_t>(kb) : j - p.K - 1 >= static_cast<uint32_t>(kb))
@@ -131,6 +128,17 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   const double S = wave_sum(sd);
   if (threadIdx.x % kWave == 0)
     p.part[(static_cast<long>(row) * p.nch1 + chunk) * kWaves + threadIdx.x / kWave] = make_float2(M, static_cast<float>(S));
+  // Block 0 also resets the state the kernels after this one fill.  It does
+  // so last, so that no workgroup's loads wait behind it.
+  if (blockIdx.x == 0) {
+    if (threadIdx.x == 0) p.qcount[0] = 0u;  // the fp64 draw's queue
+    if (p.split > 1) {  // the split fast draw: counts to zero, published values to NaN ("not yet")
+      for (int i = threadIdx.x; i < p.nseq; i += kBlock) p.vcount[p.seq0 + i] = 0u;
+      const long nsegs = static_cast<long>(p.nseq) * p.nseg, nsums = static_cast<long>(p.nseq) * kMaxSplit * 2;
+      for (long i = threadIdx.x; i < nsegs; i += kBlock) p.segm[static_cast<long>(p.seq0) * p.nseg + i] = NAN;
+      for (long i = threadIdx.x; i < nsums; i += kBlock) p.spq[static_cast<long>(p.seq0) * kMaxSplit * 2 + i] = NAN;
+    }
+  }
 }
 
 template <int DT, bool VEC, bool LARGE>
@@ -178,16 +186,19 @@ hipError_t launch_evented(Kern k, const dim3& grid, hipStream_t st, hipEvent_t e
   return hipGetLastError();
 }
 
+template <int DT, bool RAGGED>
+hipError_t launch_lse(const Params& p, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  if (!p.vec) return launch_evented(k_sweep_lse<DT, false, false, RAGGED>, grid, st, e0, e1, p);
+  if (p.sweep_large) return launch_evented(k_sweep_lse<DT, true, true, RAGGED>, grid, st, e0, e1, p);
+  return launch_evented(k_sweep_lse<DT, true, false, RAGGED>, grid, st, e0, e1, p);
+}
+
 hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const long rows = static_cast<long>(p.nseq) * (2 * p.K + 1);
   const dim3 grid(static_cast<unsigned>(rows * p.nch1));
-  const bool L = p.sweep_large != 0;
-  if (dtype == 1) return !p.vec ? launch_evented(k_sweep_lse<1, false, false>, grid, st, e0, e1, p)
-                         : L ? launch_evented(k_sweep_lse<1, true, true>, grid, st, e0, e1, p)
-                             : launch_evented(k_sweep_lse<1, true, false>, grid, st, e0, e1, p);
-  return !p.vec ? launch_evented(k_sweep_lse<0, false, false>, grid, st, e0, e1, p)
-         : L ? launch_evented(k_sweep_lse<0, true, true>, grid, st, e0, e1, p)
-             : launch_evented(k_sweep_lse<0, true, false>, grid, st, e0, e1, p);
+  const bool ragged = p.kb != nullptr;
+  if (dtype == 1) return ragged ? launch_lse<1, true>(p, grid, st, e0, e1) : launch_lse<1, false>(p, grid, st, e0, e1);
+  return ragged ? launch_lse<0, true>(p, grid, st, e0, e1) : launch_lse<0, false>(p, grid, st, e0, e1);
 }
 
 hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
