@@ -36,6 +36,64 @@ __device__ inline const void* sweep_row(const Params& p, uint32_t row) {
                                          : row_ptr<DT>(p.lq, static_cast<long>(s) * p.K + (j - p.K - 1), p.V);
 }
 
+// Slot j of sequence s, for the ragged sweep: both candidate addresses are
+// formed and one is selected, so the two base pointers load with the other
+// kernel arguments.
+template <int DT>
+__device__ inline const void* sweep_row(const Params& p, uint32_t s, uint32_t j) {
+  const void* t = row_ptr<DT>(p.lp, static_cast<long>(s) * (p.K + 1) + j, p.V);
+  const void* d = row_ptr<DT>(p.lq, static_cast<long>(s) * p.K + (static_cast<long>(j) - p.K - 1), p.V);
+  return j <= static_cast<uint32_t>(p.K) ? t : d;
+}
+
+// Where a workgroup's chunk lies.  Ragged launches (per-sequence draft
+// counts) use a grid of (chunks, row slots, sequences): no divisions, which
+// matters there because the workgroups of skipped rows only test a count
+// and leave (143.8 -> 131.7 us per ragged step at the headline shape).  The
+// others keep a one-dimensional grid over (row, chunk), which measured
+// faster for full sweeps (150.8 against 152.4 us, and 193.7 against 196.3
+// for the arg-max sweep), with the prologue they were tuned with: a shorter
+// one, without the never-true test of the counts, measured 0.3-0.8 us
+// slower per step (its loads start earlier).
+struct SweepPos {
+  uint32_t chunk, row;  // row: the launch-wide row index (sequence * slots + slot)
+  uint32_t seq, j;      // ragged only: the sequence and the row's slot in it
+};
+
+template <bool RAGGED>
+__device__ inline SweepPos sweep_pos(const Params& p, uint32_t slots) {
+  SweepPos q;
+  if constexpr (RAGGED) {
+    q.chunk = blockIdx.x;
+    q.j = blockIdx.y;
+    q.seq = static_cast<uint32_t>(p.seq0) + blockIdx.z;
+    q.row = q.seq * slots + q.j;
+  } else {
+    const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);
+    q.chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
+    q.row = static_cast<uint32_t>(p.seq0) * slots + local;
+    q.seq = q.j = 0;
+  }
+  return q;
+}
+
+// Block 0 of a launch (both grid shapes).
+__device__ inline bool first_block() { return (blockIdx.x | blockIdx.y | blockIdx.z) == 0; }
+
+// Block 0 of the sampling sweep resets, for the launch's sequences, the
+// state that the kernels after it fill: the fp64 draw's queue counter and,
+// when the fast draw is split, its per-sequence counts (0) and published
+// values (NaN: "not yet").
+__device__ inline void reset_state(const Params& p) {
+  if (threadIdx.x == 0) p.qcount[0] = 0u;
+  if (p.split > 1) {
+    for (int i = threadIdx.x; i < p.nseq; i += kBlock) p.vcount[p.seq0 + i] = 0u;
+    const long nsegs = static_cast<long>(p.nseq) * p.nseg, nsums = static_cast<long>(p.nseq) * kMaxSplit * 2;
+    for (long i = threadIdx.x; i < nsegs; i += kBlock) p.segm[static_cast<long>(p.seq0) * p.nseg + i] = NAN;
+    for (long i = threadIdx.x; i < nsums; i += kBlock) p.spq[static_cast<long>(p.seq0) * kMaxSplit * 2 + i] = NAN;
+  }
+}
+
 // This lane's elements of chunk `chunk` of a row (units of 16 bytes when VEC,
 // single elements otherwise), loaded without branches.  Bit i of `live` says
 // whether slot i lies inside the chunk.  VEC: units are addressed from the
@@ -83,24 +141,34 @@ template <int DT, bool VEC, bool LARGE, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   constexpr int N = kSweepElems<DT, VEC, false, LARGE>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);
-  const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
-  const uint32_t row = static_cast<uint32_t>(p.seq0) * (2u * p.K + 1u) + local;
-  // Per-sequence draft counts: rows past a sequence's own are not read.  The
-  // test comes before any store of this kernel, so the compiler may read the
-  // count with a scalar load, which later workgroups find in the scalar cache.
-  // (Block 0 holds a sequence's target row 0, which is always read.)
+  const SweepPos q = sweep_pos<RAGGED>(p, 2u * p.K + 1u);
+  const uint32_t chunk = q.chunk, row = q.row;
+  // Per-sequence draft counts: rows past a sequence's own are not read.  In
+  // the ragged kernel the test comes before any store, so the compiler may
+  // read the count with a scalar load, which later workgroups find in the
+  // scalar cache, and block 0 resets the state at its end (it holds a
+  // sequence's target row 0, which is always read).  The one-dimensional
+  // kernel keeps the order it was tuned with: reset first, then a test of
+  // the counts, which is never true as launched (see sweep_pos).
   if constexpr (RAGGED) {
-    const uint32_t per_seq = 2u * p.K + 1u, s = row / per_seq, j = row - s * per_seq;
-    const int kb = seq_kb(p, s);
-    if (j <= static_cast<uint32_t>(p.K) ? j > static_cast<uint32_t>(kb) : j - p.K - 1 >= static_cast<uint32_t>(kb))
+    const int kb = seq_kb(p, q.seq);
+    if (q.j <= static_cast<uint32_t>(p.K) ? q.j > static_cast<uint32_t>(kb) : q.j - p.K - 1 >= static_cast<uint32_t>(kb))
       return;
+  } else {
+    if (first_block()) reset_state(p);
+    if (p.kb) {
+      const uint32_t per_seq = 2u * p.K + 1u, s = row / per_seq, j = row - s * per_seq;
+      const int kb = seq_kb(p, s);
+      if (j <= static_cast<uint32_t>(p.K) ? j > static_cast<uint32_t>(kb) : j - p.K - 1 >= static_cast<uint32_t>(kb))
+        return;
+    }
   }
   const float c = p.c;
   float e[N];
   uint32_t live;
   long lo, hi;
-  load_chunk<DT, VEC, false, LARGE>(p, sweep_row<DT>(p, row), chunk, e, live, lo, hi);
+  const void* r = RAGGED ? sweep_row<DT>(p, q.seq, q.j) : sweep_row<DT>(p, row);
+  load_chunk<DT, VEC, false, LARGE>(p, r, chunk, e, live, lo, hi);
 
   float m = -INFINITY;
 #pragma unroll
@@ -128,27 +196,19 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   const double S = wave_sum(sd);
   if (threadIdx.x % kWave == 0)
     p.part[(static_cast<long>(row) * p.nch1 + chunk) * kWaves + threadIdx.x / kWave] = make_float2(M, static_cast<float>(S));
-  // Block 0 also resets the state the kernels after this one fill.  It does
-  // so last, so that no workgroup's loads wait behind it.
-  if (blockIdx.x == 0) {
-    if (threadIdx.x == 0) p.qcount[0] = 0u;  // the fp64 draw's queue
-    if (p.split > 1) {  // the split fast draw: counts to zero, published values to NaN ("not yet")
-      for (int i = threadIdx.x; i < p.nseq; i += kBlock) p.vcount[p.seq0 + i] = 0u;
-      const long nsegs = static_cast<long>(p.nseq) * p.nseg, nsums = static_cast<long>(p.nseq) * kMaxSplit * 2;
-      for (long i = threadIdx.x; i < nsegs; i += kBlock) p.segm[static_cast<long>(p.seq0) * p.nseg + i] = NAN;
-      for (long i = threadIdx.x; i < nsums; i += kBlock) p.spq[static_cast<long>(p.seq0) * kMaxSplit * 2 + i] = NAN;
-    }
-  }
+  if (RAGGED && first_block()) reset_state(p);
 }
 
-template <int DT, bool VEC, bool LARGE>
+template <int DT, bool VEC, bool LARGE, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
   constexpr int N = kSweepElems<DT, VEC, true, LARGE>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);  // target rows only: s * (K+1) + k
-  const uint32_t chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
-  const uint32_t row = static_cast<uint32_t>(p.seq0) * (p.K + 1u) + local;
-  if (p.kb) {  // target rows past a sequence's own draft count are not read
+  const SweepPos q = sweep_pos<RAGGED>(p, p.K + 1u);  // target rows only
+  const uint32_t chunk = q.chunk, row = q.row;
+  // target rows past a sequence's own draft count are not read
+  if constexpr (RAGGED) {
+    if (q.j > static_cast<uint32_t>(seq_kb(p, q.seq))) return;
+  } else if (p.kb) {  // never true as launched; see sweep_pos
     const uint32_t s = row / (p.K + 1u), j = row - s * (p.K + 1u);
     if (j > static_cast<uint32_t>(seq_kb(p, s))) return;
   }
@@ -186,31 +246,53 @@ hipError_t launch_evented(Kern k, const dim3& grid, hipStream_t st, hipEvent_t e
   return hipGetLastError();
 }
 
+// Ragged grids are (chunks, row slots, sequences), at most kMaxGridZ
+// sequences per launch, so larger batches are swept in slices (events, when
+// given, bracket all of them); the others are one-dimensional.
+constexpr long kMaxGridZ = 65535;
+
+template <typename Kern>
+hipError_t launch_grid(Kern k, bool ragged, unsigned slots, const Params& p, hipStream_t st, hipEvent_t e0,
+                       hipEvent_t e1) {
+  if (!ragged)
+    return launch_evented(k, dim3(static_cast<unsigned>(static_cast<long>(p.nseq) * slots * p.nch1)), st, e0, e1, p);
+  Params q = p;
+  for (long s0 = 0; s0 < p.nseq; s0 += kMaxGridZ) {
+    q.seq0 = static_cast<int>(p.seq0 + s0);
+    q.nseq = static_cast<int>(p.nseq - s0 < kMaxGridZ ? p.nseq - s0 : kMaxGridZ);
+    const dim3 grid(static_cast<unsigned>(p.nch1), slots, static_cast<unsigned>(q.nseq));
+    const hipError_t r = launch_evented(k, grid, st, s0 == 0 ? e0 : nullptr, s0 + kMaxGridZ >= p.nseq ? e1 : nullptr, q);
+    if (r != hipSuccess) return r;
+  }
+  return hipSuccess;
+}
+
 template <int DT, bool RAGGED>
-hipError_t launch_lse(const Params& p, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  if (!p.vec) return launch_evented(k_sweep_lse<DT, false, false, RAGGED>, grid, st, e0, e1, p);
-  if (p.sweep_large) return launch_evented(k_sweep_lse<DT, true, true, RAGGED>, grid, st, e0, e1, p);
-  return launch_evented(k_sweep_lse<DT, true, false, RAGGED>, grid, st, e0, e1, p);
+hipError_t launch_lse(const Params& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const unsigned slots = 2u * static_cast<unsigned>(p.K) + 1u;
+  if (!p.vec) return launch_grid(k_sweep_lse<DT, false, false, RAGGED>, RAGGED, slots, p, st, e0, e1);
+  if (p.sweep_large) return launch_grid(k_sweep_lse<DT, true, true, RAGGED>, RAGGED, slots, p, st, e0, e1);
+  return launch_grid(k_sweep_lse<DT, true, false, RAGGED>, RAGGED, slots, p, st, e0, e1);
+}
+
+template <int DT, bool RAGGED>
+hipError_t launch_argmax(const Params& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const unsigned slots = static_cast<unsigned>(p.K) + 1u;
+  if (!p.vec) return launch_grid(k_sweep_argmax<DT, false, false, RAGGED>, RAGGED, slots, p, st, e0, e1);
+  if (p.sweep_large) return launch_grid(k_sweep_argmax<DT, true, true, RAGGED>, RAGGED, slots, p, st, e0, e1);
+  return launch_grid(k_sweep_argmax<DT, true, false, RAGGED>, RAGGED, slots, p, st, e0, e1);
 }
 
 hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  const long rows = static_cast<long>(p.nseq) * (2 * p.K + 1);
-  const dim3 grid(static_cast<unsigned>(rows * p.nch1));
   const bool ragged = p.kb != nullptr;
-  if (dtype == 1) return ragged ? launch_lse<1, true>(p, grid, st, e0, e1) : launch_lse<1, false>(p, grid, st, e0, e1);
-  return ragged ? launch_lse<0, true>(p, grid, st, e0, e1) : launch_lse<0, false>(p, grid, st, e0, e1);
+  if (dtype == 1) return ragged ? launch_lse<1, true>(p, st, e0, e1) : launch_lse<1, false>(p, st, e0, e1);
+  return ragged ? launch_lse<0, true>(p, st, e0, e1) : launch_lse<0, false>(p, st, e0, e1);
 }
 
 hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  const long rows = static_cast<long>(p.nseq) * (p.K + 1);
-  const dim3 grid(static_cast<unsigned>(rows * p.nch1));
-  const bool L = p.sweep_large != 0;
-  if (dtype == 1) return !p.vec ? launch_evented(k_sweep_argmax<1, false, false>, grid, st, e0, e1, p)
-                         : L ? launch_evented(k_sweep_argmax<1, true, true>, grid, st, e0, e1, p)
-                             : launch_evented(k_sweep_argmax<1, true, false>, grid, st, e0, e1, p);
-  return !p.vec ? launch_evented(k_sweep_argmax<0, false, false>, grid, st, e0, e1, p)
-         : L ? launch_evented(k_sweep_argmax<0, true, true>, grid, st, e0, e1, p)
-             : launch_evented(k_sweep_argmax<0, true, false>, grid, st, e0, e1, p);
+  const bool ragged = p.kb != nullptr;
+  if (dtype == 1) return ragged ? launch_argmax<1, true>(p, st, e0, e1) : launch_argmax<1, false>(p, st, e0, e1);
+  return ragged ? launch_argmax<0, true>(p, st, e0, e1) : launch_argmax<0, false>(p, st, e0, e1);
 }
 
 }  // namespace sv
