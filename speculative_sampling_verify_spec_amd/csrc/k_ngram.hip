@@ -6,14 +6,16 @@
 // For a history h[0..L), an occurrence of the size-n suffix ends at e
 // (1 <= e <= L - 1, so a token follows it) where h[e-n..e) == h[L-n..L).
 // Ends are visited in rounds of 4096, sixteen per thread; a round's tokens and
-// the 16 before them are staged in LDS by coalesced loads (the next round's
-// loads issued before this round's work).  Each thread first compares the
-// last token of its ends with the suffix's (one compare per end, a bit mask);
-// size 1 is counted from the mask, and only the ends that passed go on to the
-// remaining comparisons, whose run of matches m(e) is counted for every size
-// n <= m(e) in per-thread registers (count and latest end per size, compiled
-// for the largest size in use); waves reduce them and LDS atomics gather one
-// value per wave.
+// the 16 before them are staged in LDS from registers filled by coalesced
+// loads.  The loads of the first four rounds (histories up to 16385 tokens)
+// all go out before the first round, so that rounds do not wait for memory
+// one after another; longer histories load their later rounds one at a time.
+// Each thread first compares the last token of its ends with the suffix's
+// (one compare per end, a bit mask); size 1 is counted from the mask, and
+// only the ends that passed go on to the remaining comparisons, whose run of
+// matches m(e) is counted for every size n <= m(e) in per-thread registers
+// (count and latest end per size, compiled for the largest size in use);
+// DPP wave reductions and LDS atomics gather one value per wave.
 // Thread 0 takes the largest n in [n_min, n_max] seen at least min_hits
 // times, and the workgroup writes h[e*..min(e* + K, L)) for its latest end
 // e*, then -1 up to K.  Without such an n the proposal is empty.
@@ -27,6 +29,7 @@ namespace {
 constexpr int kNgBlock = 256;
 constexpr int kNgPer = 16;                       // ends per thread per round
 constexpr int kNgRound = kNgBlock * kNgPer;
+constexpr int kNgPre = 4;                        // rounds loaded before the first (histories up to 16385 tokens)
 
 template <int NM>
 __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const int32_t* lengths, int Lmax,
@@ -34,71 +37,81 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
                                                     int32_t* out_draft, int32_t* out_count) {
   const long b = blockIdx.x;
   const int32_t* h = hist + b * static_cast<long>(Lmax);
-  const int L = min(max(lengths[b], 0), Lmax);
-  const int lane = threadIdx.x % kWave;
-  __shared__ int32_t suf[SPECV_MAX_NGRAM];  // suf[j] = h[L-1-j]
+  const int t = static_cast<int>(threadIdx.x);
+  const int lane = t % kWave;
+  const int L_raw = lengths[b];
+  // Memory order: every load the rounds use is issued before the first
+  // round, so no round waits for memory once the one before it is done.
+  // All history loads are branch-free (indices clamped; tokens at or past L,
+  // and before the history, are never counted): a load under a branch makes
+  // the compiler wait for every load in flight.
+  //  - round 0's tokens right away, clamped into the row (L_max), so they
+  //    need not wait for the length;
+  //  - the suffix, the same for every lane, by scalar loads, which are
+  //    counted apart from the vector loads (waiting for it does not wait for
+  //    the tokens);
+  //  - the tokens of rounds 1 .. kNgPre - 1, clamped to the last token.
+  int32_t v[kNgPre][kNgPer], hv[kNgPre];  // round pr's tokens h[pr * kNgRound + r * kNgBlock + t], and the NM before it
+#pragma unroll
+  for (int r = 0; r < kNgPer; ++r) v[0][r] = h[min(r * kNgBlock + t, Lmax - 1)];
+  hv[0] = 0;  // before the history
+  const int L = min(max(L_raw, 0), Lmax);
+  const int last_tok = max(L - 1, 0);
+  int32_t sf[NM];  // sf[j] = h[L-1-j], the suffix
+#pragma unroll
+  for (int j = 0; j < NM; ++j) {
+    const int32_t x = h[max(L - 1 - j, 0)];
+    sf[j] = j < L ? x : 0;
+  }
+#pragma unroll
+  for (int pr = 1; pr < kNgPre; ++pr) {
+#pragma unroll
+    for (int r = 0; r < kNgPer; ++r) v[pr][r] = h[min(pr * kNgRound + r * kNgBlock + t, last_tok)];
+    hv[pr] = h[min(max(pr * kNgRound - NM + t, 0), last_tok)];  // used by threads < NM
+  }
   __shared__ int cnt[SPECV_MAX_NGRAM + 1], last[SPECV_MAX_NGRAM + 1];
   __shared__ int s_e;
-  if (threadIdx.x < SPECV_MAX_NGRAM) suf[threadIdx.x] = threadIdx.x < L ? h[L - 1 - threadIdx.x] : 0;
-  if (threadIdx.x <= SPECV_MAX_NGRAM) {
-    cnt[threadIdx.x] = 0;
-    last[threadIdx.x] = -1;
+  if (t <= SPECV_MAX_NGRAM) {  // published by the barriers below
+    cnt[t] = 0;
+    last[t] = -1;
   }
-  __syncthreads();
   const int jmax = min(n_max, L);  // the suffix has L tokens at most; n_max <= NM
-  int32_t sf[NM];                  // the suffix in registers (the same for every lane)
-#pragma unroll
-  for (int j = 0; j < NM; ++j) sf[j] = suf[j];
   int c[NM], l[NM];  // per size n + 1: ends seen, the latest one (ends increase along a thread's walk)
 #pragma unroll
   for (int n = 0; n < NM; ++n) {
     c[n] = 0;
     l[n] = -1;
   }
-  // rounds of kNgRound ends; the round's tokens and the NM before them are
-  // staged in LDS (coalesced loads), so matches are measured without
-  // dependent global loads
+  // One round: ends base .. base + kNgRound - 1, from the thread's tokens vr
+  // (vr[r] = h[base - 1 + r * kNgBlock + t]) and hvr (the NM tokens before
+  // the round, threads < NM), staged in LDS so that matches are measured
+  // without dependent global loads.
   __shared__ int32_t win[kNgRound + SPECV_MAX_NGRAM];
-  // this round's tokens (from base - 1 on) and the NM before them, loaded one
-  // round ahead so that the loads of round r + 1 overlap the work of round r
-  auto fetch = [&](int base, int32_t (&v)[kNgPer], int32_t& hv) {
-#pragma unroll
-    for (int r = 0; r < kNgPer; ++r) {
-      const int i = base - 1 + r * kNgBlock + threadIdx.x;  // >= 0
-      v[r] = i < L ? h[i] : 0;
-    }
-    const int i = base - 1 - NM + static_cast<int>(threadIdx.x);
-    hv = (threadIdx.x < NM && i >= 0 && i < L) ? h[i] : 0;
-  };
-  int32_t v[kNgPer], hv = 0;
-  if (L > 1) fetch(1, v, hv);
-  for (int base = 1; base < L; base += kNgRound) {
+  auto round = [&](int base, const int32_t (&vr)[kNgPer], int32_t hvr) {
     const int w0 = base - 1 - NM;  // win[k] = h[w0 + k]
-    int32_t nv[kNgPer], nhv = 0;
-    if (base + kNgRound < L) fetch(base + kNgRound, nv, nhv);  // uniform
     __syncthreads();  // the previous round is done with win
 #pragma unroll
-    for (int r = 0; r < kNgPer; ++r) win[NM + r * kNgBlock + threadIdx.x] = v[r];
-    if (threadIdx.x < NM) win[threadIdx.x] = hv;
+    for (int r = 0; r < kNgPer; ++r) win[NM + r * kNgBlock + t] = vr[r];
+    if (t < NM) win[t] = hvr;
     __syncthreads();
     // first tokens: bit r of `first` says whether end r's last token equals
     // the suffix's (m(e) >= 1: e < L, and the suffix has a token); that token,
-    // h[e - 1], is the thread's own v[r]
+    // h[e - 1], is the thread's own vr[r]
     uint32_t first = 0;
 #pragma unroll
     for (int r = 0; r < kNgPer; ++r) {
-      const int e = base + r * kNgBlock + threadIdx.x;
-      first |= ((e < L && jmax > 0 && v[r] == sf[0]) ? 1u : 0u) << r;
+      const int e = base + r * kNgBlock + t;
+      first |= ((e < L && jmax > 0 && vr[r] == sf[0]) ? 1u : 0u) << r;
     }
     // size 1 straight from the bits (ends increase with r)
     c[0] += __popc(first);
-    if (first) l[0] = base + (31 - __clz(first)) * kNgBlock + threadIdx.x;
+    if (first) l[0] = base + (31 - __clz(first)) * kNgBlock + t;
     // longer sizes: only the ends whose last token matched, in increasing order
     uint32_t more = NM > 1 ? first : 0u;
     while (more) {
       const int r = __builtin_ctz(more);
       more &= more - 1u;
-      const int e = base + r * kNgBlock + threadIdx.x;
+      const int e = base + r * kNgBlock + t;
       const int k = e - 1 - w0;
       // match length m(e): trailing ones of the NM comparisons (j = 0 matched),
       // cut to the sizes that exist (j < jmax and h[e-1-j] inside the history)
@@ -113,19 +126,26 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
         l[n] = m > n ? e : l[n];
       }
     }
+  };
 #pragma unroll
-    for (int r = 0; r < kNgPer; ++r) v[r] = nv[r];
-    hv = nhv;
+  for (int pr = 0; pr < kNgPre; ++pr) {
+    const int base = 1 + pr * kNgRound;
+    if (base < L) round(base, v[pr], hv[pr]);  // uniform
   }
+  // histories longer than kNgPre rounds: the rest, one round at a time
+  for (int base = 1 + kNgPre * kNgRound; base < L; base += kNgRound) {
+    int32_t vt[kNgPer];
+#pragma unroll
+    for (int r = 0; r < kNgPer; ++r) vt[r] = h[min(base - 1 + r * kNgBlock + t, L - 1)];
+    round(base, vt, h[min(max(base - 1 - NM + t, 0), L - 1)]);
+  }
+  // per size: the wave's count and latest end (DPP reductions, lane 63 holds
+  // the result), one LDS atomic per wave
 #pragma unroll
   for (int n = 0; n < NM; ++n) {
     if (n < n_max) {  // uniform
-      int cs = c[n], ls = l[n];
-#pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) {
-        cs += __shfl_xor(cs, o, kWave);
-        ls = max(ls, __shfl_xor(ls, o, kWave));
-      }
+      const int cs = wave_reduce_i32(c[n], [](int a, int x) { return a + x; });
+      const int ls = wave_reduce_i32(l[n], [](int a, int x) { return max(a, x); });
       if (lane == 0 && cs > 0) {
         atomicAdd(&cnt[n + 1], cs);
         atomicMax(&last[n + 1], ls);
