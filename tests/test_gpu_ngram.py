@@ -20,7 +20,8 @@ def _run(gpu_lib, hist, lens, n_min, n_max, hits, K):
 
 
 @pytest.mark.parametrize("B,L,vocab,n_min,n_max,hits,K", [(64, 4096, 32000, 1, 4, 1, 5), (32, 20000, 500, 2, 8, 2, 8),
-                                                          (16, 300, 3, 1, 16, 3, 32), (128, 2048, 50000, 3, 3, 1, 1)],
+                                                          (16, 300, 3, 1, 16, 3, 32), (128, 2048, 50000, 3, 3, 1, 1),
+                                                          (8, 40000, 1000, 1, 4, 1, 5)],
                          ids=lambda x: str(x))
 def test_proposals_match_oracle(gpu_lib, B, L, vocab, n_min, n_max, hits, K):
     hist, lens = workloads.make_histories(B, L, vocab, seed=L + vocab, workers=workloads.default_workers())
