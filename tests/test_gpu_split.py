@@ -58,6 +58,8 @@ CASES = {
     "headline-100": lambda: workloads.make_batch(2, seqs=range(100), workers=workloads.default_workers()),
     "sharp-fp32-8": lambda: workloads.make_batch(3, seqs=range(8), workers=workloads.default_workers()),
     "scalar-odd-V-4": lambda: workloads.make_batch(1, wl=scalar_workload(), workers=workloads.default_workers()),
+    "k32-4": lambda: workloads.make_batch(1, wl=workloads.Workload("k32", 4, 32, 65536, "bf16", float(np.float32(0.9)),
+                                                                    2.0, 1.1, "noise", 0.6)),
     "headline-32-ragged": lambda: dataclasses.replace(
         workloads.make_batch(2, seqs=range(32), workers=workloads.default_workers()),
         num_drafts=workloads.ragged_draft_counts(32, 8, seed=7, low=0)),
