@@ -1,5 +1,6 @@
 """GPU parity of the n-gram (prompt-lookup) proposer against oracle.ngram:
 bit-exact drafts and counts."""
+import os
 import sys
 
 import numpy as np
@@ -39,5 +40,30 @@ def test_edge_lengths(gpu_lib):
     lens = np.concatenate([np.arange(0, 20), rng.integers(0, L + 1, 18), [L, L + 50]]).astype(np.int32)
     d, c = _run(gpu_lib, hist, lens, 1, 5, 1, 6)
     rd, rc = ngram.propose(hist, np.minimum(lens, L), 1, 5, 1, 6)
+    np.testing.assert_array_equal(c, rc)
+    np.testing.assert_array_equal(d, rd)
+
+
+N_RANDOM = int(os.environ.get("SPECV_RANDOM_NGRAM_CASES", "12"))
+
+
+@pytest.mark.parametrize("case", range(N_RANDOM))
+def test_random_proposals_match_oracle(gpu_lib, case):
+    # shapes on both sides of the four preloaded rounds (16385 tokens), all n
+    # ranges, small and large vocabularies, padded rows with short histories
+    rng = np.random.default_rng(7000 + case)
+    B = int(rng.integers(1, 17))
+    L = int(rng.choice([5, 100, 4097, 8193, 16385, 16386, 24000]))
+    vocab = int(rng.choice([2, 7, 300, 32000]))
+    n_max = int(rng.integers(1, 17))
+    n_min = int(rng.integers(1, n_max + 1))
+    hits = int(rng.integers(1, 4))
+    K = int(rng.integers(1, 33))
+    hist, lens = workloads.make_histories(B, L, vocab, seed=case, workers=workloads.default_workers())
+    lens = np.minimum(lens, rng.integers(0, L + 1, B)).astype(np.int32) if rng.random() < 0.3 else lens
+    print(f"[ngram-random] case {case}: B={B} L={L} vocab={vocab} n={n_min}..{n_max} hits={hits} K={K}",
+          file=sys.stderr, flush=True)
+    d, c = _run(gpu_lib, hist, lens, n_min, n_max, hits, K)
+    rd, rc = ngram.propose(hist, lens, n_min, n_max, hits, K)
     np.testing.assert_array_equal(c, rc)
     np.testing.assert_array_equal(d, rd)
