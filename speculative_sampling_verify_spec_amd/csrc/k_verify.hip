@@ -195,6 +195,16 @@ __device__ inline FastWeight fast_weight(const Params& p, const SeqRec& rec) {
   return f;
 }
 
+// A pointer that is the same in every lane, moved to scalar registers so that
+// address arithmetic on it stays scalar.
+template <class T>
+__device__ inline const T* uniform_ptr(const T* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Segment geometry of a row: units of PV elements, wave iterations of
 // 64 x U units, segments of `iters` iterations, at most kMaxSegs segments.
 template <int DT, bool VEC>
@@ -229,18 +239,20 @@ struct Iter {
   uint32_t live;            // bit i: unit i lies inside the row
 
   __device__ void load(const void* rowp, const void* rowq, long base, long units) {
-    const int lane = threadIdx.x % kWave;
+    const uint32_t lane = threadIdx.x % kWave;
     const long rem = units - base;  // > 0
+    const uint32_t in_row = static_cast<uint32_t>(rem < G::kIterUnits ? rem : G::kIterUnits);
     live = 0;
 #pragma unroll
-    for (int i = 0; i < G::U; ++i) live |= ((i * kWave + lane) < rem ? 1u : 0u) << i;
+    for (int i = 0; i < G::U; ++i) live |= ((i * kWave + lane) < in_row ? 1u : 0u) << i;
     if constexpr (VEC) {
-      const uint4* bp = static_cast<const uint4*>(rowp) + base;
-      const uint4* bq = BONUS ? nullptr : static_cast<const uint4*>(rowq) + base;
-      const uint32_t last = static_cast<uint32_t>(rem < G::kIterUnits ? rem - 1 : G::kIterUnits - 1);
+      // the iteration's base in scalar registers, a 32-bit offset per lane
+      const uint4* bp = uniform_ptr(static_cast<const uint4*>(rowp) + base);
+      const uint4* bq = BONUS ? nullptr : uniform_ptr(static_cast<const uint4*>(rowq) + base);
+      const uint32_t last = in_row - 1;
 #pragma unroll
       for (int i = 0; i < G::U; ++i) {
-        const uint32_t off = min(static_cast<uint32_t>(i * kWave + lane), last);
+        const uint32_t off = min(static_cast<uint32_t>(i * kWave) + lane, last);
         rp[i] = bp[off];
         if constexpr (!BONUS) rq[i] = bq[off];
       }
@@ -279,7 +291,7 @@ template <int DT, bool VEC, bool BONUS>
 __device__ inline void stream_row(const void* rp, const void* rq, const FastWeight& wt, const Geometry<DT, VEC>& g,
                                   int part, int split, float* segA, double& tsp, double& tsq) {
   using G = Geometry<DT, VEC>;
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave, w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   for (int j = part * kVWaves + w; j < g.nseg; j += kVWaves * split) {
     float a = 0.f;
     for (int it = 0; it < g.iters; ++it) {
@@ -434,8 +446,11 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec, int
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const G g(p.V);
   const FastWeight wt = fast_weight(p, rec);
-  const void* rp = row_ptr<DT>(p.lp, s * (p.K + 1) + rec.n, p.V);
-  const void* rq = BONUS ? nullptr : row_ptr<DT>(p.lq, s * p.K + rec.n, p.V);
+  // rec comes from LDS: make the decisive row's index wave-uniform, so the
+  // stream's addresses are formed in scalar registers
+  const int n = __builtin_amdgcn_readfirstlane(rec.n);
+  const void* rp = row_ptr<DT>(p.lp, s * (p.K + 1) + n, p.V);
+  const void* rq = BONUS ? nullptr : row_ptr<DT>(p.lq, s * p.K + n, p.V);
   __shared__ float segA[kMaxSegs];
   __shared__ double lds[kVWaves];
 
