@@ -452,13 +452,19 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec, int
   const void* rp = row_ptr<DT>(p.lp, s * (p.K + 1) + n, p.V);
   const void* rq = BONUS ? nullptr : row_ptr<DT>(p.lq, s * p.K + n, p.V);
   __shared__ float segA[kMaxSegs];
-  __shared__ double lds[kVWaves];
+  __shared__ double lds[2 * kVWaves];
 
   const int split = SPLIT ? p.split : 1;
   double tsp = 0.0, tsq = 0.0;
   stream_row<DT, VEC, BONUS>(rp, rq, wt, g, part, split, segA, tsp, tsq);
-  double SP = block_sum_n<kVWaves>(tsp, lds);  // its barriers also publish segA
-  double SQ = BONUS ? 0.0 : block_sum_n<kVWaves>(tsq, lds);
+  // the reductions' barriers also publish segA
+  double SP = tsp, SQ = 0.0;
+  if constexpr (BONUS) {
+    SP = block_sum_n<kVWaves>(tsp, lds);
+  } else {
+    SQ = tsq;
+    block_sum2_n<kVWaves>(SP, SQ, lds);
+  }
   if (w != 0) return;
 
   // segments per lane, consecutive; wave scan of the lanes' masses
