@@ -438,6 +438,29 @@ __device__ inline bool rescan_segment(const void* rp, const void* rq, const Fast
   return false;
 }
 
+// Two block sums with one pair of barriers; each is summed in the same order
+// as block_sum_n, so the results are bitwise the same.
+template <int NW>
+__device__ inline void block_sum2_n(double& a, double& b, double* lds /* >= 2 NW */) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) {
+    lds[w] = a;
+    lds[NW + w] = b;
+  }
+  __syncthreads();
+  double ta = 0.0, tb = 0.0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    ta += lds[i];
+    tb += lds[NW + i];
+  }
+  a = ta;
+  b = tb;
+}
+
 // SPLIT: the sequence's stream is shared by p.split workgroups (`part` is
 // this one's index), which exchange their results through the workspace.
 template <int DT, bool VEC, bool BONUS, bool SPLIT>
