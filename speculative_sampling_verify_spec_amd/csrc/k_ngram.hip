@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
   }
   __syncthreads();
   const int e = s_e;
-  if (threadIdx.x < K) {
+  if (static_cast<int>(threadIdx.x) < K) {
     const int i = threadIdx.x;
     out_draft[b * K + i] = (e >= 0 && e + i < L) ? h[e + i] : -1;
   }

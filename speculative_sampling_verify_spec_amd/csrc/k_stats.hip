@@ -13,14 +13,13 @@ namespace sv {
 namespace {
 
 constexpr int kStatsBlock = 1024;
-constexpr int kStatsWaves = kStatsBlock / kWave;
 constexpr int kStatsMaxBlocks = 8;
 
 __global__ __launch_bounds__(kStatsBlock) void k_position_stats(Params p) {
   __shared__ unsigned int cnt[2 * SPECV_MAX_K];
   const int lane = threadIdx.x % kWave;
   const int K = p.K;
-  if (threadIdx.x < 2 * K) cnt[threadIdx.x] = 0u;
+  if (static_cast<int>(threadIdx.x) < 2 * K) cnt[threadIdx.x] = 0u;
   __syncthreads();
   const long stride = static_cast<long>(gridDim.x) * kStatsBlock;
   const long base0 = static_cast<long>(blockIdx.x) * kStatsBlock + (threadIdx.x - lane);
@@ -39,7 +38,7 @@ __global__ __launch_bounds__(kStatsBlock) void k_position_stats(Params p) {
     }
   }
   __syncthreads();
-  if (threadIdx.x < 2 * K && cnt[threadIdx.x]) atomicAdd(&p.stats[threadIdx.x], static_cast<unsigned long long>(cnt[threadIdx.x]));
+  if (static_cast<int>(threadIdx.x) < 2 * K && cnt[threadIdx.x]) atomicAdd(&p.stats[threadIdx.x], static_cast<unsigned long long>(cnt[threadIdx.x]));
 }
 
 }  // namespace
