@@ -56,6 +56,10 @@ CASES = {
     "headline-1": lambda: workloads.make_batch(2, seqs=range(1)),
     "headline-16": lambda: workloads.make_batch(2, seqs=range(16), workers=workloads.default_workers()),
     "headline-100": lambda: workloads.make_batch(2, seqs=range(100), workers=workloads.default_workers()),
+    # both sides of the switch: the largest split batch (two workgroups per sequence on 256
+    # CUs) and the smallest batch that no longer splits
+    "headline-128": lambda: workloads.make_batch(2, seqs=range(128), workers=workloads.default_workers()),
+    "headline-129": lambda: workloads.make_batch(2, seqs=range(129), workers=workloads.default_workers()),
     "sharp-fp32-8": lambda: workloads.make_batch(3, seqs=range(8), workers=workloads.default_workers()),
     "scalar-odd-V-4": lambda: workloads.make_batch(1, wl=scalar_workload(), workers=workloads.default_workers()),
     "k32-4": lambda: workloads.make_batch(1, wl=workloads.Workload("k32", 4, 32, 65536, "bf16", float(np.float32(0.9)),
@@ -72,7 +76,7 @@ def test_split_draw_matches_oracle(gpu_lib, name):
     vec = (b.V * (2 if b.dtype == "bf16" else 4)) % 16 == 0
     split = expected_split(b.B, b.V, b.dtype, vec)
     print(f"[split] {name}: {b.wl.describe()} split={split}", file=sys.stderr, flush=True)
-    assert split > 1
+    assert split == 1 if b.B > SPLIT_MAX_SEQS else split > 1
     compare(b, run_gpu(gpu_lib, b), oracle.verify_batch(b)).check()
 
 
