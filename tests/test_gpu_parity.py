@@ -189,6 +189,28 @@ def test_bad_draft_ids_reject_and_flag(gpu_lib):
     compare(bg, run_gpu(gpu_lib, bg), oracle.verify_batch(bg)).check()
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_zero_residual_draws_from_the_target_row(gpu_lib, dtype):
+    """A rejection where the draft row equals the target row leaves max(0, p - q) = 0
+    everywhere; the draw then follows p_n (flag 2).  Reached here by an invalid draft id
+    (flag 4) at a position whose rows are identical."""
+    rng = np.random.default_rng(5)
+    B, K, V = 8, 5, 2048
+    lp = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    if dtype == "bf16":
+        lp = workloads.f32_to_bf16_bits(lp)
+    lq = lp[:, :K].copy()
+    x = rng.integers(0, V, (B, K)).astype(np.int32)
+    x[:, 2] = -1
+    ua = rng.random((B, K)).astype(np.float32)
+    ur = rng.random(B).astype(np.float32)
+    b = workloads.custom_batch(lp, lq, x, ua, ur, 0.8, dtype)
+    g = run_gpu(gpu_lib, b)
+    assert np.all(g.n == 2)
+    assert np.all(g.flags & 2) and np.all(g.flags & 4)
+    compare(b, g, oracle.verify_batch(b)).check()
+
+
 def test_determinism_and_temperature_scaling(gpu_lib):
     b = full_batch(1)
     g1 = run_gpu(gpu_lib, b)
