@@ -211,6 +211,53 @@ def test_zero_residual_draws_from_the_target_row(gpu_lib, dtype):
     compare(b, g, oracle.verify_batch(b)).check()
 
 
+def masked_batch(B, K, V, dtype, seed):
+    """Rows as after vocabulary masking, the rest -inf: every target row keeps 64 random
+    tokens; the draft row at the same position keeps 40 of them (its logits the target's
+    plus noise) and 8 tokens outside them, so the supports overlap in part.  Draft tokens
+    come from the draft row's support, except at position 1 of every other sequence, where
+    they are drawn from the whole vocabulary."""
+    rng = np.random.default_rng(seed)
+    lp = np.full((B, K + 1, V), -np.inf, np.float32)
+    lq = np.full((B, K, V), -np.inf, np.float32)
+    x = np.empty((B, K), np.int32)
+    for b in range(B):
+        for k in range(K + 1):
+            keep_p = rng.choice(V, 64, replace=False)
+            lp[b, k, keep_p] = rng.normal(0, 2, 64)
+            if k == K:
+                break
+            shared = rng.choice(keep_p, 40, replace=False)
+            lq[b, k, shared] = lp[b, k, shared] + rng.normal(0, 0.5, 40)
+            others = np.setdiff1d(rng.choice(V, 16, replace=False), keep_p)[:8]
+            lq[b, k, others] = rng.normal(0, 2, others.size)
+            keep_q = np.concatenate([shared, others])
+            x[b, k] = rng.choice(keep_q) if (k != 1 or b % 2 == 0) else rng.integers(0, V)
+    if dtype == "bf16":
+        lp, lq = workloads.f32_to_bf16_bits(lp), workloads.f32_to_bf16_bits(lq)
+    ua = rng.random((B, K)).astype(np.float32)
+    ur = rng.random(B).astype(np.float32)
+    return workloads.custom_batch(lp, lq, x, ua, ur, 0.9, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("shape", [(16, 6, 4096), (4, 4, 50001)], ids=["vector", "odd-V"])
+def test_masked_vocabulary(gpu_lib, dtype, shape):
+    """-inf logits weigh exactly 0 in the normalisers, the acceptance test and the draw."""
+    B, K, V = shape
+    b = masked_batch(B, K, V, dtype, seed=21)
+    say(f"[parity] masked {dtype} B={B} K={K} V={V}")
+    compare(b, run_gpu(gpu_lib, b), oracle.verify_batch(b)).check()
+    # greedy: sequence i copies the target's arg-max for its first i mod (K + 1) positions
+    xg = b.draft_tokens.copy()
+    for i in range(B):
+        for k in range(i % (K + 1)):
+            xg[i, k] = int(np.argmax(workloads.bf16_bits_to_f32(b.logits_p[i, k]) if dtype == "bf16"
+                                     else b.logits_p[i, k]))
+    greedy = workloads.custom_batch(b.logits_p, None, xg, None, None, 0.0, dtype)
+    compare(greedy, run_gpu(gpu_lib, greedy), oracle.verify_batch(greedy)).check()
+
+
 def test_determinism_and_temperature_scaling(gpu_lib):
     b = full_batch(1)
     g1 = run_gpu(gpu_lib, b)
