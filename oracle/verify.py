@@ -92,9 +92,10 @@ def softmax_from(y: np.ndarray, logz: np.ndarray) -> np.ndarray:
 
 
 def acceptance_threshold(log_p_x: np.ndarray, log_q_x: np.ndarray) -> np.ndarray:
-    """min(1, p(x)/q(x)) evaluated as min(1, exp(log p(x) - log q(x)))."""
-    lr = log_p_x - log_q_x
+    """min(1, p(x)/q(x)) evaluated as min(1, exp(log p(x) - log q(x))).  Where both are
+    -inf the difference is NaN, and NaN >= 0 and u < NaN are false: the draft is rejected."""
     with np.errstate(invalid="ignore", over="ignore"):
+        lr = log_p_x - log_q_x
         return np.where(lr >= 0.0, 1.0, np.exp(lr))
 
 
