@@ -17,7 +17,7 @@ import dataclasses
 
 import numpy as np
 
-from . import verify as oracle
+from .verify import Result, draw_interval
 
 NEAR_TIE = 1e-5
 BUDGET = 1e-4
@@ -47,7 +47,7 @@ class Report:
         assert self.max_logz_err <= LOGZ_TOL, f"log Z error {self.max_logz_err}"
 
 
-def compare(batch, gpu: GpuOut, ref: oracle.Result, rows: np.ndarray | None = None) -> Report:
+def compare(batch, gpu: GpuOut, ref: Result, rows: np.ndarray | None = None) -> Report:
     """Compare GPU outputs for batch rows ``rows`` (default all) with the
     oracle's results for the same sequences, in the same order."""
     rows = np.arange(batch.B) if rows is None else np.asarray(rows)
@@ -88,9 +88,9 @@ def compare(batch, gpu: GpuOut, ref: oracle.Result, rows: np.ndarray | None = No
             if not (0 <= j < batch.V):
                 failures.append((int(b), "draw out of range", j))
                 continue
-            lo, hi = oracle.draw_interval(batch.logits_p[b][: kb + 1],
-                                          None if batch.logits_q is None else batch.logits_q[b][:kb],
-                                          gn, j, float(batch.u_resample[b]), batch.T, batch.dtype)
+            lo, hi = draw_interval(batch.logits_p[b][: kb + 1],
+                                   None if batch.logits_q is None else batch.logits_q[b][:kb],
+                                   gn, j, float(batch.u_resample[b]), batch.T, batch.dtype)
             u = float(batch.u_resample[b])
             dist = 0.0 if lo <= u < hi else min(abs(u - lo), abs(u - hi))
             if dist < NEAR_TIE:
