@@ -55,7 +55,13 @@ typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype_t;
 #define SPECV_MAX_TREE     64   /* token-tree nodes: one per lane of a wave */
 #define SPECV_MAX_NGRAM    16   /* largest n-gram the prompt-lookup proposer matches */
 
-/* Flag bits of out_flags. */
+/* Flag bits of out_flags.  SPECV_FLAG_FP64 reports which path drew the
+ * token, not what was drawn: on batches of at most 128 sequences, where one
+ * sequence's draw is shared by several workgroups, a workgroup that still
+ * cannot see another's published sums after a short bounded wait hands the
+ * draw to the fp64 path, so in principle this bit may differ between two
+ * identical calls.  The tokens, the counts and the other bits never do (the
+ * fp64 path draws the same token wherever the fast one is certified). */
 #define SPECV_FLAG_FP64      1  /* the draw was made by the fp64 path: the fp32 draw could not certify its token */
 #define SPECV_FLAG_ZW_ZERO   2  /* residual mass was zero after rounding; drew from p_n instead */
 #define SPECV_FLAG_BAD_DRAFT 4  /* an evaluated draft id was outside [0, V) and was rejected */
@@ -139,9 +145,7 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
  *                drafts and accept uniforms past K_b - 1 are not read.  A
  *                sequence that accepts all K_b drafts takes its bonus token
  *                from target row K_b.  out_tokens keeps K+1 entries per
- *                sequence, -1 after the emitted token.  In sampling mode the
- *                sequence's rows of out_logz that it does not use are not
- *                written.
+ *                sequence, -1 after the emitted token.
  * position_stats [2K] uint64 (device) or NULL: counters this call adds to
  *                (the caller zeroes them once): position_stats[k] counts the
  *                sequences whose draft k was tested (k <= n and k < K_b),
@@ -157,6 +161,19 @@ int spec_verify_ragged(const void* logits_p, const void* logits_q, const int32_t
                        int B, int K, int V, int32_t* out_tokens, int32_t* out_n_accepted,
                        uint64_t* position_stats, int dtype, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * spec_verify_ragged_ex - spec_verify_ragged plus the diagnostics of
+ * spec_verify_ex: out_logz [B][2K+1] float or NULL (natural-log normalisers,
+ * K+1 target rows then K draft rows; the rows a sequence does not use, past
+ * its K_b, are not written; untouched when T == 0) and out_flags [B] int32
+ * or NULL (SPECV_FLAG_* bits).
+ */
+int spec_verify_ragged_ex(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
+                          const int32_t* num_drafts, const float* u_accept, const float* u_resample, float T,
+                          int B, int K, int V, int32_t* out_tokens, int32_t* out_n_accepted,
+                          uint64_t* position_stats, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream, float* out_logz, int32_t* out_flags);
 
 /*
  * Token trees ([A] "Token tree: kiểm nhiều nhánh đoán cùng lúc"; [C] sections

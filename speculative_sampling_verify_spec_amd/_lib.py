@@ -25,7 +25,7 @@ ERRORS = {0: "SPECV_OK", -1: "SPECV_E_NULL", -2: "SPECV_E_SHAPE", -3: "SPECV_E_D
 
 # every symbol include/specverify.h declares
 EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_ex", "spec_verify_ragged",
-           "spec_verify_tree_workspace_size", "spec_verify_tree_greedy", "spec_tree_mask", "spec_ngram_propose",
+           "spec_verify_ragged_ex", "spec_verify_tree_workspace_size", "spec_verify_tree_greedy", "spec_tree_mask", "spec_ngram_propose",
            "spec_verify_strerror", "spec_verify_version")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -57,8 +57,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify.restype = i32
     lib.spec_verify_ex.argtypes = common + [vp, vp, vp, vp]
     lib.spec_verify_ex.restype = i32
-    lib.spec_verify_ragged.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
+    ragged = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
+    lib.spec_verify_ragged.argtypes = ragged
     lib.spec_verify_ragged.restype = i32
+    lib.spec_verify_ragged_ex.argtypes = ragged + [vp, vp]
+    lib.spec_verify_ragged_ex.restype = i32
     lib.spec_verify_tree_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.spec_verify_tree_workspace_size.restype = sz
     lib.spec_verify_tree_greedy.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
@@ -122,17 +125,20 @@ def spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float
 
 def spec_verify_ragged(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T: float,
                        out_tokens=None, out_n_accepted=None, workspace=None, *, position_stats=None,
-                       stream=None) -> int:
-    """Raw call of spec_verify_ragged; returns the library's status code."""
+                       out_logz=None, out_flags=None, stream=None) -> int:
+    """Raw call of spec_verify_ragged (spec_verify_ragged_ex when log Z or
+    flags are asked for); returns the library's status code."""
     lib = load()
     B, K1, V = logits_p.shape
     import torch
     st = stream if stream is not None else torch.cuda.current_stream(logits_p.device).cuda_stream
-    return int(lib.spec_verify_ragged(_ptr(logits_p), _ptr(logits_q), _ptr(draft_tokens), _ptr(num_drafts),
-                                      _ptr(u_accept), _ptr(u_resample), float(T), B, K1 - 1, V, _ptr(out_tokens),
-                                      _ptr(out_n_accepted), _ptr(position_stats), _dtype_code(logits_p),
-                                      _ptr(workspace),
-                                      0 if workspace is None else workspace.numel() * workspace.element_size(), st))
+    args = [_ptr(logits_p), _ptr(logits_q), _ptr(draft_tokens), _ptr(num_drafts), _ptr(u_accept),
+            _ptr(u_resample), float(T), B, K1 - 1, V, _ptr(out_tokens), _ptr(out_n_accepted),
+            _ptr(position_stats), _dtype_code(logits_p), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(), st]
+    if out_logz is None and out_flags is None:
+        return int(lib.spec_verify_ragged(*args))
+    return int(lib.spec_verify_ragged_ex(*args, _ptr(out_logz), _ptr(out_flags)))
 
 
 def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
@@ -149,8 +155,9 @@ def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
 
     num_drafts [B] int32 (device) gives every sequence its own draft count
     (spec_verify_ragged); position_stats [2K] int64 (device, zeroed by the
-    caller) then receives the per-position tested / accepted counts.  Neither
-    combines with return_logz, return_flags or events."""
+    caller) then receives the per-position tested / accepted counts.  With
+    num_drafts, log Z rows a sequence does not use are NaN; events are not
+    available."""
     import torch
     dev = logits_p.device
     if dev.type != "cuda":
@@ -178,8 +185,8 @@ def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
     if num_drafts is not None:
         if num_drafts.device != dev or num_drafts.dtype != torch.int32 or tuple(num_drafts.shape) != (B,):
             raise ValueError("num_drafts must be an int32 [B] tensor on the logits' device")
-        if return_logz or return_flags or events is not None:
-            raise ValueError("num_drafts does not combine with return_logz, return_flags or events")
+        if events is not None:
+            raise ValueError("num_drafts does not combine with events")
     if position_stats is not None:
         if num_drafts is None:
             raise ValueError("position_stats needs num_drafts")
@@ -194,11 +201,13 @@ def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
-    logz = torch.empty((B, 2 * K + 1), dtype=torch.float32, device=dev) if return_logz else None
+    logz = None
+    if return_logz:  # rows a call does not write stay NaN
+        logz = torch.full((B, 2 * K + 1), float("nan"), dtype=torch.float32, device=dev)
     flags = torch.empty((B,), dtype=torch.int32, device=dev) if return_flags else None
     if num_drafts is not None:
         rc = spec_verify_ragged(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T, tokens,
-                                n_acc, workspace, position_stats=position_stats)
+                                n_acc, workspace, position_stats=position_stats, out_logz=logz, out_flags=flags)
     else:
         rc = spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T, tokens, n_acc, workspace,
                          out_logz=logz, out_flags=flags, events=events)

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
 
 #include "specverify.h"
 #include "sv_internal.h"
@@ -80,16 +81,30 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
 
 namespace {
 
+// Compute units of the current device, queried once per device (0 when the
+// device cannot be queried).
+constexpr int kMaxDevices = 64;
+
+int device_cus() {
+  static std::once_flag once[kMaxDevices];
+  static int cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::call_once(once[dev], [dev] {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? n : 0;
+  });
+  return cus[dev];
+}
+
 // Workgroups per sequence for the fast draw: one per idle CU, at most one per
 // block of kVerifyWaves segments and at most kMaxSplit; 1 for larger batches,
 // for rows of fewer than kSplitMinBlocks blocks, or if the device cannot be
 // queried.
 int verify_split(int B, int V, int dtype, bool vec) {
   if (B > kSplitMaxSeqs) return 1;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return 1;
+  const int cus = device_cus();
+  if (cus < 1) return 1;
   const int per_vec = vec ? (dtype == SPECV_BF16 ? 8 : 4) : 1;
   const SegGeom sg = seg_geom(V, per_vec, vec);
   const int blocks = (sg.nseg + kVerifyWaves - 1) / kVerifyWaves;
@@ -226,15 +241,25 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
                          ev_sweep_begin, ev_sweep_end);
 }
 
+int spec_verify_ragged_ex(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
+                          const int32_t* num_drafts, const float* u_accept, const float* u_resample, float T,
+                          int B, int K, int V, int32_t* out_tokens, int32_t* out_n_accepted,
+                          uint64_t* position_stats, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream, float* out_logz, int32_t* out_flags) {
+  if (!num_drafts) return SPECV_E_NULL;
+  return sv::verify_impl(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T, B, K, V, out_tokens,
+                         out_n_accepted, reinterpret_cast<unsigned long long*>(position_stats), dtype, workspace,
+                         workspace_bytes, stream, out_logz, out_flags, nullptr, nullptr);
+}
+
 int spec_verify_ragged(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
                        const int32_t* num_drafts, const float* u_accept, const float* u_resample, float T,
                        int B, int K, int V, int32_t* out_tokens, int32_t* out_n_accepted,
                        uint64_t* position_stats, int dtype, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  if (!num_drafts) return SPECV_E_NULL;
-  return sv::verify_impl(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T, B, K, V, out_tokens,
-                         out_n_accepted, reinterpret_cast<unsigned long long*>(position_stats), dtype, workspace,
-                         workspace_bytes, stream, nullptr, nullptr, nullptr, nullptr);
+  return spec_verify_ragged_ex(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T, B, K, V,
+                               out_tokens, out_n_accepted, position_stats, dtype, workspace, workspace_bytes, stream,
+                               nullptr, nullptr);
 }
 
 int spec_verify(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,

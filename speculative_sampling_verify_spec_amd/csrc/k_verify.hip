@@ -37,8 +37,9 @@
 //    makes the draw below.  Segment masses are the same values as unsplit.
 //    Device-wide fences (an L2 write-back and an invalidate) measured about
 //    as costly as the split's gain; instead the sweep leaves NaN in every
-//    published slot, and a NaN read back sends the sequence to the fp64 draw,
-//    so the result never depends on when the stores become visible.
+//    published slot, a NaN read back is read again a bounded number of times,
+//    and one still NaN sends the sequence to the fp64 draw, so the result
+//    never depends on when the stores become visible.
 //  - Select.  Wave 0 scans the segment masses for the segment holding t,
 //    recomputes that segment's weights and finds the token with wave scans in
 //    token order.  The answer stands when t is further from both ends of the
@@ -56,6 +57,7 @@ constexpr int kVBlock = kVerifyBlock;         // threads per workgroup
 constexpr int kVWaves = kVerifyWaves;         // 16
 constexpr int kRowsMax = 2 * SPECV_MAX_K + 1;
 constexpr int kRowsPerWave = (kRowsMax + kVWaves - 1) / kVWaves;  // 5 rows per wave at most
+constexpr int kSplitReads = 16;  // reads of the published values before the fp64 fallback
 
 // ------------------------------------------------------------ acceptance --
 // Fold one lane's (R, s) sweep partial into its running pair (ml, sl):
@@ -516,25 +518,31 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec, int
     prior = __builtin_amdgcn_readlane(prior, 0);
     if (prior != static_cast<uint32_t>(split - 1)) return;  // uniform over the wave
     // the last one: every workgroup's masses and sums (device-scope loads).
-    // A value still NaN is one whose store this workgroup cannot see yet;
-    // rather than wait, the sequence then goes to the fp64 draw, which needs
-    // none of them.  So the draw never depends on the order in which the
-    // other workgroups' stores become visible.
-    bool seen = true;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int j = lane * per + k;
-      segv[k] = (k < per && j < g.nseg) ? __hip_atomic_load(gseg + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                        : 0.f;
-      seen &= !isnan(segv[k]);
-    }
+    // Every other workgroup counted itself done only after its stores had
+    // completed, so a value still NaN is one whose store is not yet visible
+    // here: read again, a bounded number of times.  If one is still NaN the
+    // sequence goes to the fp64 draw, which needs none of them, so the draw
+    // never depends on when the other workgroups' stores become visible.
+    bool seen = false;
     double psp = 0.0, psq = 0.0;
-    if (lane < split) {
-      psp = __hip_atomic_load(gsum + 2 * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      psq = __hip_atomic_load(gsum + 2 * lane + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      seen &= !(isnan(psp) || isnan(psq));
+    for (int attempt = 0; attempt < kSplitReads && !seen; ++attempt) {  // uniform over the wave
+      if (attempt > 0) __builtin_amdgcn_s_sleep(2);
+      bool mine_seen = true;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int j = lane * per + k;
+        segv[k] = (k < per && j < g.nseg) ? __hip_atomic_load(gseg + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                          : 0.f;
+        mine_seen &= !isnan(segv[k]);
+      }
+      if (lane < split) {
+        psp = __hip_atomic_load(gsum + 2 * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        psq = __hip_atomic_load(gsum + 2 * lane + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mine_seen &= !(isnan(psp) || isnan(psq));
+      }
+      seen = __ballot(!mine_seen) == 0;
     }
-    if (__ballot(!seen)) {  // uniform
+    if (!seen) {  // uniform
       if (lane == 0) {
         if (p.out_flags) p.out_flags[s] = rec.flags | SPECV_FLAG_FP64;
         const uint32_t slot = atomicAdd(&p.qcount[0], 1u);

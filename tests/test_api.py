@@ -131,6 +131,17 @@ def test_ragged_entry_point_checks(lib):
     assert lib.spec_verify_ragged(P, None, X, KB, None, None, 0.0, 4, 3, 128, OT, ON, None, F32, WS, 16, None) == -5
 
 
+def test_ragged_ex_entry_point_checks(lib):
+    KB, LZ, FL = 0x90000, 0xA0000, 0xB0000
+    ex = lib.spec_verify_ragged_ex
+    assert ex(P, Q, X, None, UA, UR, 1.0, 4, 3, 128, OT, ON, None, F32, WS, 1 << 30, None, LZ, FL) == -1
+    assert ex(P, Q, X, KB, UA, UR, 1.0, 4, 3, 128, OT, ON, None, 7, WS, 1 << 30, None, LZ, FL) == -3
+    assert ex(P, Q, X, KB, UA, UR, float("nan"), 4, 3, 128, OT, ON, None, F32, WS, 1 << 30, None, LZ, FL) == -4
+    assert ex(P, Q, X, KB, UA, UR, 1.0, 0, 3, 128, OT, ON, None, F32, WS, 1 << 30, None, LZ, FL) == -2
+    assert ex(P, Q, X, KB, UA, UR, 1.0, 4, 3, 128, OT, ON, None, F32, WS, 16, None, LZ, FL) == -5
+    assert ex(P + 2, Q, X, KB, UA, UR, 1.0, 4, 3, 128, OT, ON, None, F32, WS, 1 << 30, None, LZ, FL) == -6
+
+
 def test_binding_checks_ragged_arguments():
     import torch
     lp = torch.zeros(2, 3, 8)
