@@ -251,10 +251,23 @@ def position_stats(n_accepted: np.ndarray, num_drafts: np.ndarray, K: int) -> np
     return np.concatenate([evaluated, accepted]).astype(np.int64)
 
 
-def verify_batch(batch, seqs: Optional[np.ndarray] = None) -> Result:
-    """Convenience wrapper for a ``workloads.Batch``-like object."""
-    return verify(batch.logits_p, batch.logits_q, batch.draft_tokens, batch.u_accept,
-                  batch.u_resample, batch.T, batch.dtype, seqs, getattr(batch, "num_drafts", None))
+def verify_batch(batch, seqs: Optional[np.ndarray] = None, workers: int = 1) -> Result:
+    """Convenience wrapper for a ``workloads.Batch``-like object.  With
+    workers > 1 the sequences are split into that many contiguous parts run in
+    threads (numpy's array operations release the interpreter lock); the
+    result is the same as one pass."""
+    idx = np.arange(batch.B) if seqs is None else np.asarray(seqs)
+    args = (batch.logits_p, batch.logits_q, batch.draft_tokens, batch.u_accept, batch.u_resample, batch.T,
+            batch.dtype)
+    nd = getattr(batch, "num_drafts", None)
+    if workers <= 1 or len(idx) < 2:
+        return verify(*args, idx, nd)
+    from concurrent.futures import ThreadPoolExecutor
+    parts = [p for p in np.array_split(idx, min(workers, len(idx))) if len(p)]
+    with ThreadPoolExecutor(len(parts)) as ex:
+        res = list(ex.map(lambda p: verify(*args, p, nd), parts))
+    return Result(**{f.name: np.concatenate([getattr(r, f.name) for r in res])
+                     for f in dataclasses.fields(Result)})
 
 
 def draw_interval(logits_p_seq, logits_q_seq, n: int, j: int, u: float, T: float, dtype: str):

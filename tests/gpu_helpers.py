@@ -6,18 +6,17 @@ from oracle.parity import GpuOut
 
 
 def run_gpu(sv, batch, dev_inputs=None, position_stats=None) -> GpuOut:
-    """The HIP path on a batch; a batch with per-sequence draft counts goes
-    through spec_verify_ragged (no log Z or flags: those fields are None)."""
+    """The HIP path on a batch, with log Z (sampling mode) and flags; a batch
+    with per-sequence draft counts goes through spec_verify_ragged_ex."""
     import torch
     lp, lq, x, ua, ur = dev_inputs if dev_inputs is not None else workloads.to_device(batch)
     greedy = batch.T == 0.0
     nd = getattr(batch, "num_drafts", None)
+    kb = None
     if nd is not None:
         kb = torch.from_numpy(np.ascontiguousarray(nd, dtype=np.int32)).to(lp.device)
-        tok, n = sv.verify(lp, lq, x, ua, ur, batch.T, num_drafts=kb, position_stats=position_stats)
-        torch.cuda.synchronize()
-        return GpuOut(tok.cpu().numpy(), n.cpu().numpy(), None, None)
-    out = sv.verify(lp, lq, x, ua, ur, batch.T, return_logz=not greedy, return_flags=True)
+    out = sv.verify(lp, lq, x, ua, ur, batch.T, return_logz=not greedy, return_flags=True, num_drafts=kb,
+                    position_stats=position_stats)
     torch.cuda.synchronize()
     if greedy:
         tok, n, flags = out

@@ -1,11 +1,12 @@
 """GPU parity: the HIP path against the fp64 oracle, through the C ABI.
 
-Sizes: the five workloads at full size (the large sharp fp32 one is checked
-against the oracle on a sample of its sequences), small odd shapes that
+Sizes: the five workloads at full size (every sequence of each, the large
+sharp fp32 one generated in blocks), small odd shapes that
 exercise ragged tails and the scalar path, and special cases.
 """
 import dataclasses
 import sys
+import types
 
 import numpy as np
 import pytest
@@ -44,53 +45,91 @@ def test_workload_full_size(gpu_lib, cfg):
     rep.check()
 
 
-def _one(blk, i, s):
-    """Sequence i of a generated block as a batch of one (sequence id s)."""
-    return workloads.Batch(wl=dataclasses.replace(blk.wl, B=1), cfg_id=blk.cfg_id, seqs=np.array([s]),
-                           logits_p=blk.logits_p[i:i + 1], logits_q=blk.logits_q[i:i + 1],
-                           draft_tokens=blk.draft_tokens[i:i + 1], u_accept=blk.u_accept[i:i + 1],
-                           u_resample=blk.u_resample[i:i + 1])
+_SHARP = {}
 
 
-def test_sharp_fp32_workload_full_size_sampled(gpu_lib):
-    """B=1024, K=4, V=256000 fp32 (9.4 GB of logits) generated in blocks
-    straight into device memory; the oracle checks every 16th sequence."""
+def sharp_blocks(step=64):
+    """The sharp workload (B=1024, K=4, V=256000, fp32: 9.4 GB of logits) as
+    host blocks of `step` sequences, generated once per session."""
+    if "blocks" not in _SHARP:
+        wl = workloads.WORKLOADS[3]
+        blocks = []
+        for s0 in range(0, wl.B, step):
+            blocks.append(workloads.make_batch(3, seqs=range(s0, s0 + step), workers=workloads.default_workers()))
+            say(f"[parity] workload 3: generated {s0 + step}/{wl.B}")
+        _SHARP["blocks"] = blocks
+    return _SHARP["blocks"]
+
+
+def sharp_on_device(blocks):
+    """Copy the blocks into one set of device tensors [B, ...]."""
     import torch
     wl = workloads.WORKLOADS[3]
     B, K, V = wl.B, wl.K, wl.V
-    say(f"[parity] workload 3 {wl.describe()} (generating in blocks)")
     lp = torch.empty((B, K + 1, V), dtype=torch.float32, device="cuda")
     lq = torch.empty((B, K, V), dtype=torch.float32, device="cuda")
     x = torch.empty((B, K), dtype=torch.int32, device="cuda")
     ua = torch.empty((B, K), dtype=torch.float32, device="cuda")
     ur = torch.empty((B,), dtype=torch.float32, device="cuda")
-    kept = {}
-    step = 64
-    for s0 in range(0, B, step):
-        blk = workloads.make_batch(3, seqs=range(s0, s0 + step), workers=workloads.default_workers())
-        lp[s0:s0 + step], lq[s0:s0 + step], x[s0:s0 + step], ua[s0:s0 + step], ur[s0:s0 + step] = to_device(blk)
-        for i in range(0, step, 16):
-            kept[s0 + i] = _one(blk, i, s0 + i)
-        if s0 + step == B:
-            kept[B - 1] = _one(blk, step - 1, B - 1)
-        say(f"[parity] workload 3: generated {s0 + step}/{B}")
-    g = run_gpu(gpu_lib, wl, dev_inputs=(lp, lq, x, ua, ur))
-    fails, exc, dec, lz = [], 0, 0, 0.0
-    for s, one in sorted(kept.items()):
-        gs = dataclasses.replace(g, tokens=g.tokens[s:s + 1], n=g.n[s:s + 1], logz=g.logz[s:s + 1],
-                                 flags=g.flags[s:s + 1])
-        rep = compare(one, gs, oracle.verify_batch(one))
-        fails += rep.failures
+    s0 = 0
+    for blk in blocks:
+        s1 = s0 + blk.B
+        lp[s0:s1], lq[s0:s1], x[s0:s1], ua[s0:s1], ur[s0:s1] = to_device(blk)
+        s0 = s1
+    return lp, lq, x, ua, ur
+
+
+def compare_blocks(blocks, g, num_drafts=None):
+    """Every sequence of every block against the oracle (threads per block)."""
+    fails, exc, dec, lz, s0 = [], 0, 0, 0.0, 0
+    for blk in blocks:
+        s1 = s0 + blk.B
+        if num_drafts is not None:
+            blk = dataclasses.replace(blk, num_drafts=num_drafts[s0:s1])
+        gs = dataclasses.replace(g, tokens=g.tokens[s0:s1], n=g.n[s0:s1], logz=g.logz[s0:s1], flags=g.flags[s0:s1])
+        rep = compare(blk, gs, oracle.verify_batch(blk, workers=workloads.default_workers()))
+        fails += [(f[0] + s0,) + tuple(f[1:]) for f in rep.failures]
         exc += rep.excused
         dec += rep.decisions
         lz = max(lz, rep.max_logz_err)
-    say(f"[parity] workload 3 sample of {len(kept)}: decisions={dec} excused={exc} max_logz_err={lz:.2e}")
+        s0 = s1
+    return fails, exc, dec, lz
+
+
+def test_sharp_fp32_workload_full_size(gpu_lib):
+    """B=1024, K=4, V=256000 fp32: every one of the 1024 sequences against the
+    oracle (tokens, counts, log Z of all 9 rows)."""
+    blocks = sharp_blocks()
+    say("[parity] workload 3: copying to the device")
+    dev = sharp_on_device(blocks)
+    g = run_gpu(gpu_lib, workloads.WORKLOADS[3], dev_inputs=dev)
+    del dev
+    fails, exc, dec, lz = compare_blocks(blocks, g)
+    say(f"[parity] workload 3, all {len(g.n)} sequences: decisions={dec} excused={exc} max_logz_err={lz:.2e}")
     assert not fails, fails[:3]
     assert exc <= 1e-4 * dec
     assert lz <= 1e-5
-    assert np.all((g.n >= 0) & (g.n <= K))
-    emitted = g.tokens[np.arange(B), g.n]
-    assert np.all((emitted >= 0) & (emitted < V))
+
+
+def test_sharp_fp32_workload_full_size_ragged(gpu_lib):
+    """The same 1024 sequences with per-sequence draft counts K_b uniform on
+    [0, 4] through spec_verify_ragged_ex (its large sweep shape, the unsplit
+    fast draw), log Z of the rows each sequence uses included."""
+    import torch
+    blocks = sharp_blocks()
+    wl = workloads.WORKLOADS[3]
+    kb = workloads.ragged_draft_counts(wl.B, wl.K, seed=31, low=0)
+    say(f"[parity] workload 3 ragged: K_b from {kb.min()} to {kb.max()}")
+    dev = sharp_on_device(blocks)
+    st = torch.zeros(2 * wl.K, dtype=torch.int64, device="cuda")
+    g = run_gpu(gpu_lib, types.SimpleNamespace(T=wl.T, num_drafts=kb), dev_inputs=dev, position_stats=st)
+    del dev
+    fails, exc, dec, lz = compare_blocks(blocks, g, num_drafts=kb)
+    say(f"[parity] workload 3 ragged: decisions={dec} excused={exc} max_logz_err={lz:.2e}")
+    assert not fails, fails[:3]
+    assert exc <= 1e-4 * dec
+    assert lz <= 1e-5
+    np.testing.assert_array_equal(st.cpu().numpy(), oracle.position_stats(g.n, kb, wl.K))
 
 
 @pytest.mark.parametrize("cfg", [1, 2])

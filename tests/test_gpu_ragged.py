@@ -48,6 +48,36 @@ def test_ragged_sampling_matches_oracle(gpu_lib, cfg, B, V):
     np.testing.assert_array_equal(st.cpu().numpy(), oracle.position_stats(g.n, b.num_drafts, b.K))
 
 
+@pytest.mark.parametrize("low", [0, 1])
+def test_ragged_headline_full_size(gpu_lib, low):
+    """The headline shape at full size (B=256, K=8, V=128256 bf16, T=0.7) with
+    K_b uniform on [low, 8]: the ragged sweep's large shape (21760 workgroups)
+    and the unsplit fast draw, log Z of the used rows included."""
+    b = _ragged(2, low=low, seed=41 + low)
+    say(f"[ragged] headline B={b.B} K_b from {b.num_drafts.min()} to {b.num_drafts.max()}")
+    st = _stats_tensor(b.K)
+    g = run_gpu(gpu_lib, b, position_stats=st)
+    ref = oracle.verify_batch(b, workers=workloads.default_workers())
+    rep = compare(b, g, ref)
+    say(f"[ragged] headline: decisions={rep.decisions} excused={rep.excused} max_logz_err={rep.max_logz_err:.2e}")
+    rep.check()
+    np.testing.assert_array_equal(st.cpu().numpy(), oracle.position_stats(g.n, b.num_drafts, b.K))
+
+
+def test_ragged_greedy_full_size(gpu_lib):
+    """The greedy workload at full size (B=512, K=8, V=152064 bf16) with K_b
+    uniform on [0, 8]: the ragged arg-max sweep's large shape (23040
+    workgroups), bit-exact."""
+    b = _ragged(4, seed=43)
+    say(f"[ragged] greedy B={b.B} K_b from {b.num_drafts.min()} to {b.num_drafts.max()}")
+    st = _stats_tensor(b.K)
+    g = run_gpu(gpu_lib, b, position_stats=st)
+    ref = oracle.verify_batch(b, workers=workloads.default_workers())
+    np.testing.assert_array_equal(g.n, ref.n_accepted)
+    np.testing.assert_array_equal(g.tokens, ref.tokens)
+    np.testing.assert_array_equal(st.cpu().numpy(), oracle.position_stats(ref.n_accepted, b.num_drafts, b.K))
+
+
 def test_ragged_greedy_matches_oracle(gpu_lib):
     b = _ragged(4, B=96, V=30000, seed=12)
     st = _stats_tensor(b.K)

@@ -447,3 +447,16 @@ def test_position_acceptance_rates_follow_sum_of_min():
     for k in range(K - 1):
         full = np.sum((kb == k + 1) & (r.n_accepted == k + 1))
         assert ev[k + 1] == ac[k] - full
+
+
+def test_threaded_batch_equals_one_pass():
+    """verify_batch(..., workers=N) splits the sequences over threads; the result
+    must be the one-pass result, field for field (also with draft counts)."""
+    import dataclasses
+    import workloads
+    b = workloads.make_batch(1, seqs=range(20), V=3000, seed=77)
+    for nd in (None, workloads.ragged_draft_counts(20, b.K, seed=77, low=0)):
+        bb = dataclasses.replace(b, num_drafts=nd)
+        one, many = oracle.verify_batch(bb), oracle.verify_batch(bb, workers=6)
+        for f in dataclasses.fields(oracle.Result):
+            np.testing.assert_array_equal(getattr(one, f.name), getattr(many, f.name), err_msg=f.name)
