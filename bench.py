@@ -10,13 +10,19 @@ region is K back-to-back steps between two synchronisations.  The whole
 input (1.1 GB) exceeds the 256 MB Infinity Cache, so no step is served from
 a previous step's cache.
 
+Warm-up is untimed and lasts at least --warmup steps and at least
+--ramp-seconds of them, because a freshly started GPU raises its clocks
+over about the first second; the steps it took are reported (`ramp_steps`).
+
 Prints one JSON line.  `value` and `ms_per_step` come from a first timed
-pass of K steps with nothing else in the stream.  `roofline` describes the
-dominant kernel (the row sweep): a second timed pass of K steps attaches HIP
-events to every sweep dispatch (recorded with the dispatch itself), which
-costs the step some microseconds, so that pass is reported separately
-(`ms_per_step_with_events`).  `cpu_baseline` times the fp64 oracle on a
-bounded sample of the same batch.
+pass of K steps with nothing else in the stream.  A second timed pass of K
+steps records events between steps (`step_us`: median, p10, p90, first and
+last step) and, with the sweep's dispatches, events that time the sweep
+alone (`sweep_us`); those cost the step some microseconds, so that pass's
+mean is reported separately (`ms_per_step_with_events`).  `roofline`
+describes the dominant kernel (the row sweep) from those sweep events.
+`cpu_baseline` times the fp64 oracle on the same batch on all host threads
+and on one.
 
 --copy-calibration BYTES first runs three plain device-to-device copies of
 that many bytes, so that a rocprofv3 counter pass over the same process
@@ -105,26 +111,81 @@ def counter_traffic(swept_bytes: int):
     return float(m_bytes.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """Oracle threads: the host's cores, at most 16 (one GPU's share of a
+    shared host)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def cpu_baseline(batch, gpu_tokens, gpu_n, budget_s: float):
-    """The fp64 oracle, as it stands, on the timed batch: whole passes over its
-    sequences, one thread, until about budget_s seconds are spent (at least
-    one sequence).  Also counts sequences whose GPU output differs."""
+    """The fp64 oracle, as it stands, on the timed batch, in the same run:
+    whole passes over its sequences on all host threads (numpy releases the
+    interpreter lock in its array operations), then on one thread, each for
+    about half of budget_s (at least one pass / one sequence).  The all-thread
+    rate is `value`.  Also counts sequences whose GPU output differs."""
     import numpy as np
     from oracle import verify_batch
-    done, t0 = 0, time.perf_counter()
-    mismatched = 0
-    while time.perf_counter() - t0 < budget_s or done == 0:
-        b = done % batch.B
-        r = verify_batch(batch, seqs=[b])
-        if done < batch.B and (r.n_accepted[0] != gpu_n[b] or not np.array_equal(r.tokens[0], gpu_tokens[b])):
-            mismatched += 1
+    threads = host_threads()
+    # all threads: whole passes over the batch
+    passes, mismatched, t0 = 0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s / 2 or passes == 0:
+        r = verify_batch(batch, workers=threads)
+        if passes == 0:
+            mismatched = int(np.sum((r.n_accepted != gpu_n) | np.any(r.tokens != gpu_tokens, axis=1)))
+        passes += 1
+    dt_all = time.perf_counter() - t0
+    # one thread: sequence by sequence
+    done, t1 = 0, time.perf_counter()
+    while time.perf_counter() - t1 < budget_s / 2 or done == 0:
+        verify_batch(batch, seqs=[done % batch.B])
         done += 1
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "verified seq-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} sequence verifications ({done / batch.B:.2f} passes over the timed batch of "
-                      f"{batch.B}), fp64 numpy, one thread",
-            "seconds": round(dt, 2), "sample_mismatches_vs_gpu": mismatched,
-            "sample_compared": min(done, batch.B)}
+    dt_one = time.perf_counter() - t1
+    return {"value": passes * batch.B / dt_all, "unit": "verified seq-steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} whole passes over the timed batch of {batch.B} sequences, fp64 numpy, "
+                      f"{threads} threads",
+            "seconds": round(dt_all, 2),
+            "one_thread": {"value": done / dt_one, "sample": f"{done} sequence verifications, one thread",
+                           "seconds": round(dt_one, 2)},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample_mismatches_vs_gpu": mismatched, "sample_compared": batch.B}
+
+
+def dist_us(ms) -> dict:
+    """Median, p10, p90, mean, first and last of per-step times (ms in, us out)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "mean": float(np.mean(a)), "first": float(a[0]), "last": float(a[-1]), "n": int(a.size)}
+
+
+def warm_up(step, steps: int, seconds: float):
+    """Untimed warm-up: at least `steps` steps and at least `seconds` of them
+    (the clocks of a freshly started GPU rise over the first second or so).
+    Returns the steps taken and a trace of their mean time per block."""
+    import torch
+    done, t0, trace = 0, time.perf_counter(), []
+    tb, nb = t0, 0
+    while done < steps or time.perf_counter() - t0 < seconds:
+        step()
+        done += 1
+        nb += 1
+        if nb == 200:  # bound the queue, and record how the step time settles
+            torch.cuda.synchronize()
+            now = time.perf_counter()
+            trace.append(round((now - tb) / nb * 1e6, 1))
+            tb, nb = now, 0
+    torch.cuda.synchronize()
+    return done, time.perf_counter() - t0, trace
 
 
 def tree_bench(args):
@@ -145,9 +206,12 @@ def tree_bench(args):
     par = torch.from_numpy(tb.parents).cuda()
     ws = torch.empty(int(sv.load().spec_verify_tree_workspace_size(B, N, V, sv.SPECV_BF16)), dtype=torch.uint8,
                      device="cuda")
-    for i in range(args.warmup):
-        out = sv.verify_tree_greedy(lgs[i % ncopy], tok_in, par, workspace=ws)
-    torch.cuda.synchronize()
+    turn = [0]
+
+    def warm():
+        sv.verify_tree_greedy(lgs[turn[0] % ncopy], tok_in, par, workspace=ws)
+        turn[0] += 1
+    ramp_steps, _, _ = warm_up(warm, args.warmup, args.ramp_seconds)
     t0 = time.perf_counter()
     for i in range(args.steps):
         out = sv.verify_tree_greedy(lgs[i % ncopy], tok_in, par, workspace=ws)
@@ -157,6 +221,7 @@ def tree_bench(args):
     nbytes = B * N * V * 2
     line = {"metric": "verified trees/s + HBM GB/s (% peak), greedy token trees", "value": B / step_s,
             "unit": "verified trees/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ramp_steps": ramp_steps,
             "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "f32", "data": "synthetic",
             "config": {"workload": f"tree-bf16: {B} trees of {N} nodes (chains branching with probability 1/2), "
@@ -191,9 +256,12 @@ def ngram_bench(args):
     h, ln = torch.from_numpy(hist).cuda(), torch.from_numpy(lens).cuda()
     ncopy = input_copies(h.numel() * 4)
     hs = [h] + [h.clone() for _ in range(ncopy - 1)]  # used in turn
-    for i in range(args.warmup):
-        out = sv.ngram_propose(hs[i % ncopy], ln, n_min, n_max, hits, K)
-    torch.cuda.synchronize()
+    turn = [0]
+
+    def warm():
+        sv.ngram_propose(hs[turn[0] % ncopy], ln, n_min, n_max, hits, K)
+        turn[0] += 1
+    ramp_steps, _, _ = warm_up(warm, args.warmup, args.ramp_seconds)
     t0 = time.perf_counter()
     for i in range(args.steps):
         out = sv.ngram_propose(hs[i % ncopy], ln, n_min, n_max, hits, K)
@@ -203,6 +271,7 @@ def ngram_bench(args):
     cnt = out[1].cpu().numpy()
     line = {"metric": "proposals/s + HBM GB/s (% peak), n-gram prompt lookup", "value": B / step_s,
             "unit": "proposals/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ramp_steps": ramp_steps,
             "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "int32", "data": "synthetic",
             "config": {"workload": f"ngram: {B} histories, lengths uniform in [{L // 2}, {L}], vocab {vocab}, "
@@ -231,6 +300,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--ramp-seconds", type=float, default=2.0,
+                    help="untimed warm-up lasts at least this long, whatever --warmup says (clock ramp)")
     ap.add_argument("--workload", type=int, default=HEADLINE, choices=range(5))
     ap.add_argument("--seqs", type=int, default=0, metavar="N",
                     help="verify only the first N sequences of the workload (a smaller batch of the same shape)")
@@ -313,24 +384,27 @@ def main():
         if rc != 0:
             raise RuntimeError(sv.strerror(rc))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"warm; timing {args.steps} steps")
+    ramp_steps, ramp_s, ramp_trace = warm_up(step, args.warmup, args.ramp_seconds)
+    log(f"warm after {ramp_steps} steps ({ramp_s:.2f}s; us per step by blocks of 200: {ramp_trace[:12]}"
+        f"{' ...' if len(ramp_trace) > 12 else ''}); timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sweep_ms, wall_ev = None, None
-    if not args.ragged:
-        log(f"timing {args.steps} steps with events on the sweep")
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(ev.pairs[i])
-        torch.cuda.synchronize()
-        wall_ev = time.perf_counter() - t0
-        sweep_ms = [ev.elapsed_ms(i) for i in range(args.steps)]
+    # a second pass of K steps: events between steps (per-step times) and,
+    # outside ragged mode, events recorded with the sweep's dispatches
+    log(f"timing {args.steps} steps with events")
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    bounds[0].record()
+    for i in range(args.steps):
+        step(None if args.ragged else ev.pairs[i])
+        bounds[i + 1].record()
+    torch.cuda.synchronize()
+    wall_ev = time.perf_counter() - t0
+    step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]
+    sweep_ms = None if args.ragged else [ev.elapsed_ms(i) for i in range(args.steps)]
     ev.close()
 
     n_host = n_acc.cpu().numpy()
@@ -346,7 +420,10 @@ def main():
         "unit": "verified seq-steps/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": step_s * 1e3,
-        "ms_per_step_with_events": None if wall_ev is None else wall_ev / args.steps * 1e3,
+        "ms_per_step_with_events": wall_ev / args.steps * 1e3,
+        "ramp_steps": ramp_steps, "ramp_seconds": round(ramp_s, 3),
+        "step_us": dist_us(step_ms),
+        "sweep_us": None if sweep_ms is None else dist_us(sweep_ms),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{wl.name}: verify {batch.wl.describe()}, logits {batch.dtype}"
