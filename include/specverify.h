@@ -50,10 +50,12 @@ typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype_t;
 #define SPECV_E_WORKSPACE  -5   /* workspace NULL, misaligned, or smaller than required */
 #define SPECV_E_ALIGN      -6   /* a logits pointer is not aligned to its element size */
 #define SPECV_E_HIP        -7   /* a kernel launch failed */
+#define SPECV_E_SCRATCH    -8   /* spec_verify_noalloc: the shape needs more than SPECV_NOALLOC_SCRATCH bytes */
 
 #define SPECV_MAX_K        32   /* one 64-lane wave runs the acceptance scan */
 #define SPECV_MAX_TREE     64   /* token-tree nodes: one per lane of a wave */
 #define SPECV_MAX_NGRAM    16   /* largest n-gram the prompt-lookup proposer matches */
+#define SPECV_NOALLOC_SCRATCH (32u << 20)  /* bytes of spec_verify_noalloc's static scratch per device */
 
 /* Flag bits of out_flags.  SPECV_FLAG_FP64 reports which path drew the
  * token, not what was drawn: on batches of at most 128 sequences, where one
@@ -114,6 +116,25 @@ int spec_verify(const void* logits_p, const void* logits_q, const int32_t* draft
                 const float* u_accept, const float* u_resample, float T, int B, int K, int V,
                 int32_t* out_tokens, int32_t* out_n_accepted, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_noalloc - spec_verify for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without a workspace, the same kernels and
+ * results.  Its scratch is a static device array of SPECV_NOALLOC_SCRATCH
+ * bytes that the library holds on each device it runs on until the process
+ * ends; its address is looked up on the first call on a device.  Shapes
+ * whose workspace (spec_verify_workspace_size) exceeds it return
+ * SPECV_E_SCRATCH with nothing enqueued; the five workloads of this library's
+ * tests need at most about 16 MB.  It calls no allocator.  Every call on one
+ * device shares that scratch: calls that may overlap on one device (other
+ * streams, other threads) race and must be serialised by the caller.  Each
+ * call resets what it needs inside its own kernels, so no clearing is
+ * required between calls.
+ */
+int spec_verify_noalloc(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
+                        const float* u_accept, const float* u_resample, float T, int B, int K, int V,
+                        int32_t* out_tokens, int32_t* out_n_accepted, int dtype, void* stream);
 
 /*
  * spec_verify_ex - spec_verify plus diagnostics for tests and benchmarks.

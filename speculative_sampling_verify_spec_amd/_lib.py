@@ -21,10 +21,12 @@ SPECV_MAX_NGRAM = 16
 FLAG_FP64, FLAG_ZW_ZERO, FLAG_BAD_DRAFT = 1, 2, 4
 
 ERRORS = {0: "SPECV_OK", -1: "SPECV_E_NULL", -2: "SPECV_E_SHAPE", -3: "SPECV_E_DTYPE", -4: "SPECV_E_TEMP",
-          -5: "SPECV_E_WORKSPACE", -6: "SPECV_E_ALIGN", -7: "SPECV_E_HIP"}
+          -5: "SPECV_E_WORKSPACE", -6: "SPECV_E_ALIGN", -7: "SPECV_E_HIP", -8: "SPECV_E_SCRATCH"}
+NOALLOC_SCRATCH = 32 << 20
 
 # every symbol include/specverify.h declares
-EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_ex", "spec_verify_ragged",
+EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_noalloc", "spec_verify_ex",
+           "spec_verify_ragged",
            "spec_verify_ragged_ex", "spec_verify_tree_workspace_size", "spec_verify_tree_greedy", "spec_tree_mask", "spec_ngram_propose",
            "spec_verify_strerror", "spec_verify_version")
 
@@ -55,6 +57,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     common = [vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, i32, vp, sz, vp]
     lib.spec_verify.argtypes = common
     lib.spec_verify.restype = i32
+    lib.spec_verify_noalloc.argtypes = common[:12] + [vp]
+    lib.spec_verify_noalloc.restype = i32
     lib.spec_verify_ex.argtypes = common + [vp, vp, vp, vp]
     lib.spec_verify_ex.restype = i32
     ragged = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
@@ -121,6 +125,19 @@ def spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float
         return int(lib.spec_verify(*args))
     e0, e1 = events if events is not None else (None, None)
     return int(lib.spec_verify_ex(*args, _ptr(out_logz), _ptr(out_flags), e0, e1))
+
+
+def spec_verify_noalloc(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, out_tokens,
+                        out_n_accepted, *, stream=None) -> int:
+    """Raw call of spec_verify_noalloc (no workspace: the library's static
+    scratch); returns the library's status code."""
+    lib = load()
+    B, K1, V = logits_p.shape
+    import torch
+    st = stream if stream is not None else torch.cuda.current_stream(logits_p.device).cuda_stream
+    return int(lib.spec_verify_noalloc(_ptr(logits_p), _ptr(logits_q), _ptr(draft_tokens), _ptr(u_accept),
+                                       _ptr(u_resample), float(T), B, K1 - 1, V, _ptr(out_tokens),
+                                       _ptr(out_n_accepted), _dtype_code(logits_p), st))
 
 
 def spec_verify_ragged(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T: float,

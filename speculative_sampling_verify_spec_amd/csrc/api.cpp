@@ -10,6 +10,13 @@
 #include "specverify.h"
 #include "sv_internal.h"
 
+// Scratch of spec_verify_noalloc: the workspace of a call that cannot
+// allocate, in device memory the library holds on every device it runs on
+// until the process ends.  In host code `scratch` names a host-side stand-in;
+// its device address comes from hipGetSymbolAddress (scratch_ptr below).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace sv {
 
 namespace {
@@ -85,6 +92,20 @@ namespace {
 // device cannot be queried).
 constexpr int kMaxDevices = 64;
 
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current; null if the lookup fails.
+void* scratch_ptr() {
+  static std::once_flag once[kMaxDevices];
+  static void* ptr[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(once[dev], [dev] {
+    void* q = nullptr;
+    ptr[dev] = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) == hipSuccess ? q : nullptr;
+  });
+  return ptr[dev];
+}
+
 int device_cus() {
   static std::once_flag once[kMaxDevices];
   static int cus[kMaxDevices];
@@ -152,7 +173,7 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
                 const float* u_accept, const float* u_resample, float T, int B, int K, int V,
                 int32_t* out_tokens, int32_t* out_n_accepted, unsigned long long* position_stats, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream, float* out_logz, int32_t* out_flags,
-                void* ev_sweep_begin, void* ev_sweep_end) {
+                void* ev_sweep_begin, void* ev_sweep_end, size_t* need = nullptr) {
   if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_E_DTYPE;
   if (!valid_temperature(T)) return SPECV_E_TEMP;
   const bool greedy = T == 0.f;
@@ -165,6 +186,7 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   if (ap % eb || aq % eb) return SPECV_E_ALIGN;
   const bool vec = ap % 16 == 0 && aq % 16 == 0 && (static_cast<long>(V) * eb) % 16 == 0;
   const Layout L = make_layout(B, K, V, dtype, vec, greedy);
+  if (need) *need = L.total;
   if (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign || workspace_bytes < L.total)
     return SPECV_E_WORKSPACE;
 
@@ -239,6 +261,23 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   return sv::verify_impl(logits_p, logits_q, draft_tokens, nullptr, u_accept, u_resample, T, B, K, V, out_tokens,
                          out_n_accepted, nullptr, dtype, workspace, workspace_bytes, stream, out_logz, out_flags,
                          ev_sweep_begin, ev_sweep_end);
+}
+
+int spec_verify_noalloc(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
+                        const float* u_accept, const float* u_resample, float T, int B, int K, int V,
+                        int32_t* out_tokens, int32_t* out_n_accepted, int dtype, void* stream) {
+  // every argument check of spec_verify first (no workspace: it stops there)
+  size_t need = 0;
+  const int rc = sv::verify_impl(logits_p, logits_q, draft_tokens, nullptr, u_accept, u_resample, T, B, K, V,
+                                 out_tokens, out_n_accepted, nullptr, dtype, nullptr, 0, stream, nullptr, nullptr,
+                                 nullptr, nullptr, &need);
+  if (rc != SPECV_E_WORKSPACE) return rc;
+  if (need > kScratchBytes) return SPECV_E_SCRATCH;
+  void* ws = sv::scratch_ptr();
+  if (!ws) return SPECV_E_HIP;
+  return sv::verify_impl(logits_p, logits_q, draft_tokens, nullptr, u_accept, u_resample, T, B, K, V, out_tokens,
+                         out_n_accepted, nullptr, dtype, ws, kScratchBytes, stream, nullptr, nullptr, nullptr,
+                         nullptr);
 }
 
 int spec_verify_ragged_ex(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
@@ -365,6 +404,7 @@ const char* spec_verify_strerror(int code) {
     case SPECV_E_WORKSPACE: return "workspace NULL, not 256-byte aligned, or too small";
     case SPECV_E_ALIGN: return "logits pointer not aligned to its element size";
     case SPECV_E_HIP: return "a HIP launch failed";
+    case SPECV_E_SCRATCH: return "the shape needs more than the 32 MiB static scratch of spec_verify_noalloc";
     default: return "unknown error";
   }
 }

@@ -177,3 +177,30 @@ def test_ngram_entry_point_checks_arguments(lib):
     for bad in [dict(B=0), dict(L=0), dict(nmin=0), dict(nmin=3, nmax=2), dict(nmax=17), dict(hits=0),
                 dict(K=0), dict(K=33)]:
         assert call(**bad) == -2, bad
+
+
+def test_noalloc_entry_point_checks(lib):
+    """spec_verify_noalloc runs spec_verify's host-side checks, and rejects a
+    shape whose workspace exceeds its static scratch before any HIP call."""
+    na = lib.spec_verify_noalloc
+    assert na(None, Q, X, UA, UR, 1.0, 4, 3, 128, OT, ON, F32, None) == -1
+    assert na(P, None, X, UA, UR, 1.0, 4, 3, 128, OT, ON, F32, None) == -1
+    assert na(P, Q, X, UA, UR, 1.0, 4, 3, 128, OT, ON, 9, None) == -3
+    assert na(P, Q, X, UA, UR, -2.0, 4, 3, 128, OT, ON, F32, None) == -4
+    assert na(P, Q, X, UA, UR, 1.0, 4, 40, 128, OT, ON, F32, None) == -2
+    assert na(P + 2, Q, X, UA, UR, 1.0, 4, 3, 128, OT, ON, F32, None) == -6
+    # 4096 sequences of the sharp shape need far more than 32 MiB of workspace
+    assert sv.workspace_size(4096, 4, 256000, F32, 1.0) > sv.NOALLOC_SCRATCH
+    assert na(P, Q, X, UA, UR, 1.0, 4096, 4, 256000, OT, ON, F32, None) == -8
+    assert na(P, None, X, None, None, 0.0, 65536, 32, 256000, OT, ON, BF16, None) == -8
+    # the five workloads fit
+    for B, K, V, dt, T in [(1, 4, 1000, F32, 1.0), (64, 5, 32000, BF16, 1.0), (256, 8, 128256, BF16, 0.7),
+                           (1024, 4, 256000, F32, 1.0), (512, 8, 152064, BF16, 0.0)]:
+        assert sv.workspace_size(B, K, V, dt, T) <= sv.NOALLOC_SCRATCH
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+SPECV_NOALLOC_SCRATCH\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == sv.NOALLOC_SCRATCH
+    assert "SPECV_E_SCRATCH" in sv.ERRORS.values()
