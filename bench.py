@@ -55,6 +55,9 @@ def input_copies(nbytes: int) -> int:
     step is served from what the previous use of its input left there."""
     return max(2, -(-2 * LLC_BYTES // max(nbytes, 1)) + 1)
 HEADLINE = 2
+# The library's sweep rounds (levels [0, 1), [1, 3), [3, K + 1)) unless every
+# row's log Z is asked for; used here only to count the bytes a step reads.
+ROUND_BEGINS = (0, 1, 3)
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "sweep_lse_headline_counters.md")
 # the sweep kernel's source: its file and the headers it includes (hashed in this order)
 SWEEP_SOURCES = [os.path.join(ROOT, "speculative_sampling_verify_spec_amd", "csrc", f)
@@ -158,6 +161,28 @@ def cpu_baseline(batch, gpu_tokens, gpu_n, budget_s: float):
                            "seconds": round(dt_one, 2)},
             "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample_mismatches_vs_gpu": mismatched, "sample_compared": batch.B}
+
+
+def rows_per_step(n, kb, K: int, greedy: bool, full: bool):
+    """Logit rows one step reads (the sweep only), and the rows the method
+    needs: levels 0..n of each sequence (target row k, and draft row k below
+    K_b), n its accepted count.  The full sweep reads every row up to K_b; the
+    rounds read a round's rows for every sequence that reached it (no
+    rejection before its first level)."""
+    import numpy as np
+    n, kb = np.asarray(n, np.int64), np.asarray(kb, np.int64)
+    drafts = 0 if greedy else 1
+    needed = int(np.sum((n + 1) + drafts * np.minimum(n + 1, kb)))
+    if full:
+        return int(np.sum((kb + 1) + drafts * kb)), needed
+    bounds = [b for b in ROUND_BEGINS if b <= K] + [K + 1]
+    read = 0
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        reached = n >= a
+        t = np.clip(np.minimum(b - 1, kb) - a + 1, 0, None)
+        d = np.clip(np.minimum(b, kb) - a, 0, None)
+        read += int(np.sum(np.where(reached, t + drafts * d, 0)))
+    return read, needed
 
 
 def dist_us(ms) -> dict:
@@ -312,6 +337,8 @@ def main():
                     help="greedy token-tree verification: 128 trees of 32 nodes, V=128256 bf16")
     ap.add_argument("--ngram", action="store_true",
                     help="prompt-lookup proposer: 1024 histories of up to 16384 tokens, n = 1..4, K = 5")
+    ap.add_argument("--full", action="store_true",
+                    help="ask for every row's log Z, which sweeps every row at once instead of in rounds")
     ap.add_argument("--ragged", action="store_true",
                     help="per-sequence draft counts K_b uniform on [1, K] (spec_verify_ragged with "
                          "per-position counters); bytes count the rows actually read")
@@ -360,6 +387,7 @@ def main():
     tokens = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
     n_acc = torch.empty((B,), dtype=torch.int32, device="cuda")
     flags = torch.empty((B,), dtype=torch.int32, device="cuda")
+    logz = torch.empty((B, 2 * K + 1), dtype=torch.float32, device="cuda") if args.full else None
     ev = HipEvents(args.steps)
 
     kb_host = workloads.ragged_draft_counts(B, K) if args.ragged else None
@@ -378,9 +406,11 @@ def main():
         cp, cq = copies[turn[0] % ncopy]
         turn[0] += 1
         if args.ragged:
-            rc = sv.spec_verify_ragged(cp, cq, x, kb, ua, ur, T, tokens, n_acc, ws, position_stats=stats)
+            rc = sv.spec_verify_ragged(cp, cq, x, kb, ua, ur, T, tokens, n_acc, ws, position_stats=stats,
+                                       out_logz=logz)
         else:
-            rc = sv.spec_verify(cp, cq, x, ua, ur, T, tokens, n_acc, ws, out_flags=flags, events=e, extended=True)
+            rc = sv.spec_verify(cp, cq, x, ua, ur, T, tokens, n_acc, ws, out_flags=flags, out_logz=logz, events=e,
+                                extended=True)
         if rc != 0:
             raise RuntimeError(sv.strerror(rc))
 
@@ -410,8 +440,9 @@ def main():
     n_host = n_acc.cpu().numpy()
     tok_host = tokens.cpu().numpy()
     kbs = kb_host if args.ragged else np.full(B, K)
-    rows_swept = int(np.sum(kbs + 1)) if greedy else int(np.sum(2 * kbs + 1))
-    swept = rows_swept * V * elt
+    rows_read, rows_needed = rows_per_step(n_host, kbs, K, greedy, args.full)
+    rows_all = int(np.sum(kbs + 1)) if greedy else int(np.sum(2 * kbs + 1))
+    swept, needed, swept_all = (r * V * elt for r in (rows_read, rows_needed, rows_all))
     reread = 0 if greedy else int(np.sum(np.where(n_host < kbs, 2, 1))) * V * elt
     step_s = wall / args.steps
     line = {
@@ -428,11 +459,18 @@ def main():
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{wl.name}: verify {batch.wl.describe()}, logits {batch.dtype}"
                                + (f" (the first {B} sequences of the {wl.B})" if args.seqs else "")
-                               + (", per-sequence draft counts uniform on [1, K]" if args.ragged else ""),
+                               + (", per-sequence draft counts uniform on [1, K]" if args.ragged else "")
+                               + (", every row's log Z (one sweep of every row)" if args.full else ""),
                    "B": B, "K": K, "V": V, "logits": batch.dtype, "T": T, "parallelism": "none (one GPU)"},
-        "hbm_gbps_algorithmic": (swept + reread) / step_s / 1e9,
+        # bytes the step reads from HBM (rows swept + decisive rows reread)
+        "hbm_gbps": (swept + reread) / step_s / 1e9,
         "hbm_frac_of_peak": (swept + reread) / step_s / 1e9 / PEAK_HBM_GBS,
-        "bytes_per_step": {"swept": swept, "decisive_reread": reread},
+        # every logit once + the reread (the byte count the headline metric
+        # names), per step time: above peak when rows past a rejection are skipped
+        "hbm_gbps_all_rows_model": (swept_all + reread) / step_s / 1e9,
+        "bytes_per_step": {"swept": swept, "decisive_reread": reread, "rows_swept": rows_read,
+                           "needed": needed, "rows_needed": rows_needed, "all_rows": swept_all,
+                           "rows_all": rows_all},
         "mean_accepted": float(np.mean(n_host)),
         "input_copies": ncopy,
         "fp64_draw_fraction": None if (greedy or args.ragged) else float(np.mean((flags.cpu().numpy() & sv.FLAG_FP64) != 0)),
@@ -450,6 +488,7 @@ def main():
                             # the committed counters cover the log-sum-exp sweep only
                             "traffic": None if greedy else counter_traffic(swept),
                             "launch_us": sweep_s * 1e6, "launches_timed": args.steps,
+                            "sweep_launches_per_step": 1 if args.full else len([b for b in ROUND_BEGINS if b <= K]),
                             "algorithmic_bytes_per_launch": swept}
     if not args.no_cpu_baseline:
         log(f"timing the fp64 oracle on a sample (~{args.cpu_seconds:.0f}s)")

@@ -133,6 +133,32 @@ int verify_split(int B, int V, int dtype, bool vec) {
   return std::max(1, std::min(std::min(cus / B, blocks), kMaxSplit));
 }
 
+// The sweep's launches for one call: every row at once when `full` (the
+// caller asked for every row's normaliser), else rounds of levels (see
+// kMaxProLevels), each launch's events given to the first and last.
+hipError_t launch_sweeps(Params P, int dtype, bool greedy, bool full, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  auto launch = [&](const Params& q, hipEvent_t a, hipEvent_t b) {
+    return greedy ? launch_sweep_argmax(q, dtype, st, a, b) : launch_sweep_lse(q, dtype, st, a, b);
+  };
+  if (full) {
+    P.grid3 = P.kb ? 1 : 0;  // per-sequence counts need the 3-D grid
+    P.lv0 = 0;
+    P.lv1 = P.K + 1;
+    return launch(P, e0, e1);
+  }
+  int bounds[kMaxRounds + 1], nr = 0;
+  for (int r = 0; r < kMaxRounds && round_begin(r) <= P.K; ++r) bounds[nr++] = round_begin(r);
+  bounds[nr] = P.K + 1;
+  P.grid3 = 1;
+  for (int r = 0; r < nr; ++r) {
+    P.lv0 = bounds[r];
+    P.lv1 = bounds[r + 1];
+    const hipError_t rc = launch(P, r == 0 ? e0 : nullptr, r == nr - 1 ? e1 : nullptr);
+    if (rc != hipSuccess) return rc;
+  }
+  return hipSuccess;
+}
+
 bool valid_temperature(float T) {
   if (!std::isfinite(T) || T < 0.f) return false;
   if (T == 0.f) return true;
@@ -219,8 +245,10 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   hipEvent_t e0 = static_cast<hipEvent_t>(ev_sweep_begin), e1 = static_cast<hipEvent_t>(ev_sweep_end);
   const bool timed = e0 && e1;
 
+  // every row's normaliser asked for: one sweep of every row; else rounds
+  const bool full = out_logz != nullptr;
   if (greedy) {
-    if (launch_sweep_argmax(P, dtype, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
+    if (launch_sweeps(P, dtype, true, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
       return SPECV_E_HIP;
     if (launch_greedy_scan(P, st) != hipSuccess) return SPECV_E_HIP;
     if (position_stats && launch_position_stats(P, st) != hipSuccess) return SPECV_E_HIP;
@@ -243,7 +271,8 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   P.spq = reinterpret_cast<double*>(ws + L.spq);
   P.vcount = reinterpret_cast<uint32_t*>(ws + L.vcount);
 
-  if (launch_sweep_lse(P, dtype, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess) return SPECV_E_HIP;
+  if (launch_sweeps(P, dtype, false, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
+    return SPECV_E_HIP;
   if (launch_verify(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   if (launch_exact(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   if (position_stats && launch_position_stats(P, st) != hipSuccess) return SPECV_E_HIP;

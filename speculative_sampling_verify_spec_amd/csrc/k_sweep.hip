@@ -17,6 +17,17 @@
 // before it computes.  A row is split into chunks of equal size, one
 // workgroup each, so no workgroup gets a short tail; each wave writes its own
 // partial, so no workgroup barrier holds finished waves back.
+//
+// Rounds.  Without a request for every row's normaliser, the sweep runs in
+// rounds of levels (see kMaxProLevels): acceptance stops at the first
+// rejection ([B] "多 Token 验证：左到右，遇错即停"), so rows past it are never
+// needed.  A round's grid is (chunks, round slots, sequences); a workgroup of
+// a later round first repeats, in every wave for itself, the acceptance
+// tests of the earlier levels from the partials already written (the same
+// fold and test as the acceptance scan after the sweep), and leaves before
+// loading anything when its sequence has rejected.  Rows of levels past a
+// rejection keep stale partials, which only ever decide tests after the
+// first failing one.
 #include <hip/hip_ext.h>
 
 #include "sv_device.h"
@@ -36,9 +47,9 @@ __device__ inline const void* sweep_row(const Params& p, uint32_t row) {
                                          : row_ptr<DT>(p.lq, static_cast<long>(s) * p.K + (j - p.K - 1), p.V);
 }
 
-// Slot j of sequence s, for the ragged sweep: both candidate addresses are
-// formed and one is selected, so the two base pointers load with the other
-// kernel arguments.
+// Row j of sequence s (target rows 0..K, then draft rows), for the 3-D grid:
+// both candidate addresses are formed and one is selected, so the two base
+// pointers load with the other kernel arguments.
 template <int DT>
 __device__ inline const void* sweep_row(const Params& p, uint32_t s, uint32_t j) {
   const void* t = row_ptr<DT>(p.lp, static_cast<long>(s) * (p.K + 1) + j, p.V);
@@ -46,35 +57,152 @@ __device__ inline const void* sweep_row(const Params& p, uint32_t s, uint32_t j)
   return j <= static_cast<uint32_t>(p.K) ? t : d;
 }
 
-// Where a workgroup's chunk lies.  Ragged launches (per-sequence draft
-// counts) use a grid of (chunks, row slots, sequences): no divisions, which
-// matters there because the workgroups of skipped rows only test a count
-// and leave (143.8 -> 131.7 us per ragged step at the headline shape).  The
-// others keep a one-dimensional grid over (row, chunk), which measured
+// Where a workgroup's chunk lies.  The 3-D grid (chunks, round slots,
+// sequences) serves rounds and per-sequence draft counts: no divisions,
+// which matters there because the workgroups of skipped rows only test a
+// count and leave (143.8 -> 131.7 us per ragged step at the headline shape).
+// Slot y < lv1 - lv0 of a round is target row lv0 + y; the rest are the
+// draft rows of the round's levels (none in the arg-max sweep).  The full
+// sweep keeps a one-dimensional grid over (row, chunk), which measured
 // faster for full sweeps (150.8 against 152.4 us, and 193.7 against 196.3
-// for the arg-max sweep), with the prologue they were tuned with: a shorter
+// for the arg-max sweep), with the prologue it was tuned with: a shorter
 // one, without the never-true test of the counts, measured 0.3-0.8 us
 // slower per step (its loads start earlier).
 struct SweepPos {
-  uint32_t chunk, row;  // row: the launch-wide row index (sequence * slots + slot)
-  uint32_t seq, j;      // ragged only: the sequence and the row's slot in it
+  uint32_t chunk, row;  // row: the launch-wide row index (sequence * rows per sequence + j)
+  uint32_t seq, j;      // 3-D grid only: the sequence and its row j (target k: k; draft k: K + 1 + k)
+  int level;            // 3-D grid only: the row's level
+  bool draft;           // 3-D grid only: a draft row
 };
 
-template <bool RAGGED>
-__device__ inline SweepPos sweep_pos(const Params& p, uint32_t slots) {
+template <bool G3, bool ARGMAX>
+__device__ inline SweepPos sweep_pos(const Params& p) {
+  const uint32_t per_seq = ARGMAX ? p.K + 1u : 2u * p.K + 1u;
   SweepPos q;
-  if constexpr (RAGGED) {
+  if constexpr (G3) {
+    const int nt = p.lv1 - p.lv0, y = static_cast<int>(blockIdx.y);
     q.chunk = blockIdx.x;
-    q.j = blockIdx.y;
     q.seq = static_cast<uint32_t>(p.seq0) + blockIdx.z;
-    q.row = q.seq * slots + q.j;
+    q.draft = !ARGMAX && y >= nt;
+    q.level = p.lv0 + (q.draft ? y - nt : y);
+    q.j = static_cast<uint32_t>(q.draft ? p.K + 1 + q.level : q.level);
+    q.row = q.seq * per_seq + q.j;
   } else {
     const uint32_t local = blockIdx.x / static_cast<uint32_t>(p.nch1);
     q.chunk = blockIdx.x - local * static_cast<uint32_t>(p.nch1);
-    q.row = static_cast<uint32_t>(p.seq0) * slots + local;
+    q.row = static_cast<uint32_t>(p.seq0) * per_seq + local;
     q.seq = q.j = 0;
+    q.level = 0;
+    q.draft = false;
   }
   return q;
+}
+
+// ------------------------------------------------ the earlier levels' tests --
+// Partials of row j of sequence s, lanes lane and lane + 64, loaded
+// branch-free (clamped index, masked afterwards) so that every row's loads
+// are in flight together.
+__device__ inline void load_row_partials(const Params& p, long s, uint32_t per_seq, int j, bool in, int np,
+                                         float2 (&q)[2], float2 empty) {
+  const int lane = threadIdx.x % kWave;
+  const float2* base = p.part + (s * per_seq + (in ? j : 0)) * np;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = lane + h * kWave;
+    const float2 v = base[i < np ? i : np - 1];
+    q[h] = (in && i < np) ? v : empty;
+  }
+}
+
+// Whether sequence s accepted its drafts at levels 0..a-1 (1 <= a <=
+// kMaxProLevels, a <= K_b), from the sweep partials of those levels' target
+// and draft rows: the acceptance scan's fold and test.  Whole wave.
+template <int DT>
+__device__ inline bool accepted_before(const Params& p, long s, int a) {
+  const int lane = threadIdx.x % kWave;
+  const int K = p.K, np = p.nch1 * kWaves;
+  const uint32_t per_seq = 2u * K + 1u;
+  // the partials of the 2a rows go out first, then draft token -> its logits
+  float2 q[2 * kMaxProLevels][2];
+#pragma unroll
+  for (int r = 0; r < kMaxProLevels; ++r) {
+    load_row_partials(p, s, per_seq, r, r < a, np, q[r], make_float2(-INFINITY, 0.f));
+    load_row_partials(p, s, per_seq, K + 1 + r, r < a, np, q[kMaxProLevels + r], make_float2(-INFINITY, 0.f));
+  }
+  const int li = lane < a ? lane : 0;
+  const int xk = p.x[s * K + li];
+  const float u = p.ua[s * K + li];
+  const bool valid = xk >= 0 && xk < p.V;
+  const int xs = valid ? xk : 0;
+  const float xp = Elt<DT>::at(row_ptr<DT>(p.lp, s * (K + 1) + li, p.V), xs);
+  const float xq = Elt<DT>::at(row_ptr<DT>(p.lq, s * K + li, p.V), xs);
+  float ml[2 * kMaxProLevels];
+  double sl[2 * kMaxProLevels];
+#pragma unroll
+  for (int r = 0; r < 2 * kMaxProLevels; ++r) {
+    ml[r] = -INFINITY;
+    sl[r] = 0.0;
+    fold_partial(ml[r], sl[r], q[r][0]);
+    fold_partial(ml[r], sl[r], q[r][1]);
+  }
+  for (int i = lane + 2 * kWave; i < np; i += kWave)  // long rows: the rest of the partials
+#pragma unroll
+    for (int r = 0; r < kMaxProLevels; ++r) {
+      if (r < a) {
+        fold_partial(ml[r], sl[r], p.part[(s * per_seq + r) * np + i]);
+        fold_partial(ml[kMaxProLevels + r], sl[kMaxProLevels + r], p.part[(s * per_seq + K + 1 + r) * np + i]);
+      }
+    }
+  double lzp = 0.0, lzq = 0.0;  // lane k: log2 Z of target row k and of draft row k
+#pragma unroll
+  for (int r = 0; r < kMaxProLevels; ++r) {
+    if (r < a) {  // uniform over the wave
+      const double zp = wave_log2z(ml[r], sl[r]);
+      const double zq = wave_log2z(ml[kMaxProLevels + r], sl[kMaxProLevels + r]);
+      if (lane == r) {
+        lzp = zp;
+        lzq = zq;
+      }
+    }
+  }
+  bool accept = false;
+  if (lane < a && valid) {
+    const double c = p.c;
+    const double lr = (static_cast<double>(xp) * c - lzp) - (static_cast<double>(xq) * c - lzq);
+    const double thr = lr >= 0.0 ? 1.0 : exp2(lr);
+    accept = static_cast<double>(u) < thr;
+  }
+  return __ballot(lane < a && !accept) == 0;
+}
+
+// Greedy: whether the drafts at levels 0..a-1 equal the first arg-max of
+// their target rows, from the arg-max sweep's partials.  Whole wave.
+__device__ inline bool matched_before(const Params& p, long s, int a) {
+  const int lane = threadIdx.x % kWave;
+  const int K = p.K, np = p.nch1 * kWaves;
+  const uint32_t per_seq = K + 1u;
+  float2 q[kMaxProLevels][2];
+#pragma unroll
+  for (int r = 0; r < kMaxProLevels; ++r)
+    load_row_partials(p, s, per_seq, r, r < a, np, q[r], make_float2(-INFINITY, __int_as_float(0x7fffffff)));
+  const int xk = p.x[s * K + (lane < a ? lane : 0)];
+  int am = -1;  // lane k: the arg-max of target row k
+#pragma unroll
+  for (int r = 0; r < kMaxProLevels; ++r) {
+    if (r < a) {  // uniform over the wave
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      argmax_merge(bv, bi, q[r][0].x, __float_as_int(q[r][0].y));
+      argmax_merge(bv, bi, q[r][1].x, __float_as_int(q[r][1].y));
+      for (int i = lane + 2 * kWave; i < np; i += kWave) {
+        const float2 v = p.part[(s * per_seq + r) * np + i];
+        argmax_merge(bv, bi, v.x, __float_as_int(v.y));
+      }
+      wave_argmax(bv, bi);
+      if (lane == r) am = bi;
+    }
+  }
+  return __ballot(lane < a && xk != am) == 0;
 }
 
 // Block 0 of a launch (both grid shapes).
@@ -135,25 +263,27 @@ __device__ inline void load_chunk(const Params& p, const void* r, uint32_t chunk
   }
 }
 
-// RAGGED: per-sequence draft counts (a separate instantiation, so that the
-// common case carries no code for them ahead of its loads).
-template <int DT, bool VEC, bool LARGE, bool RAGGED>
+// G3: the 3-D grid of rounds and per-sequence draft counts (a separate
+// instantiation, so that the full sweep carries no code for them ahead of
+// its loads).
+template <int DT, bool VEC, bool LARGE, bool G3>
 __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   constexpr int N = kSweepElems<DT, VEC, false, LARGE>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  const SweepPos q = sweep_pos<RAGGED>(p, 2u * p.K + 1u);
+  const SweepPos q = sweep_pos<G3, false>(p);
   const uint32_t chunk = q.chunk, row = q.row;
-  // Per-sequence draft counts: rows past a sequence's own are not read.  In
-  // the ragged kernel the test comes before any store, so the compiler may
-  // read the count with a scalar load, which later workgroups find in the
-  // scalar cache, and block 0 resets the state at its end (it holds a
+  // Rows past a sequence's own draft count are not read, and in a later
+  // round neither are those of a sequence that has rejected.  In the 3-D
+  // kernel the count test comes before any store, so the compiler may read
+  // the count with a scalar load, which later workgroups find in the scalar
+  // cache, and block 0 of round 0 resets the state at its end (it holds a
   // sequence's target row 0, which is always read).  The one-dimensional
   // kernel keeps the order it was tuned with: reset first, then a test of
-  // the counts, which is never true as launched (see sweep_pos).
-  if constexpr (RAGGED) {
+  // the counts, which is never true as launched.
+  if constexpr (G3) {
     const int kb = seq_kb(p, q.seq);
-    if (q.j <= static_cast<uint32_t>(p.K) ? q.j > static_cast<uint32_t>(kb) : q.j - p.K - 1 >= static_cast<uint32_t>(kb))
-      return;
+    if (q.draft ? q.level >= kb : q.level > kb) return;
+    if (p.lv0 > 0 && !accepted_before<DT>(p, q.seq, p.lv0)) return;  // uniform over the wave
   } else {
     if (first_block()) reset_state(p);
     if (p.kb) {
@@ -167,7 +297,7 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   float e[N];
   uint32_t live;
   long lo, hi;
-  const void* r = RAGGED ? sweep_row<DT>(p, q.seq, q.j) : sweep_row<DT>(p, row);
+  const void* r = G3 ? sweep_row<DT>(p, q.seq, q.j) : sweep_row<DT>(p, row);
   load_chunk<DT, VEC, false, LARGE>(p, r, chunk, e, live, lo, hi);
 
   float m = -INFINITY;
@@ -196,18 +326,20 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   const double S = wave_sum(sd);
   if (threadIdx.x % kWave == 0)
     p.part[(static_cast<long>(row) * p.nch1 + chunk) * kWaves + threadIdx.x / kWave] = make_float2(M, static_cast<float>(S));
-  if (RAGGED && first_block()) reset_state(p);
+  if (G3 && p.lv0 == 0 && first_block()) reset_state(p);
 }
 
-template <int DT, bool VEC, bool LARGE, bool RAGGED>
+template <int DT, bool VEC, bool LARGE, bool G3>
 __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
   constexpr int N = kSweepElems<DT, VEC, true, LARGE>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  const SweepPos q = sweep_pos<RAGGED>(p, p.K + 1u);  // target rows only
+  const SweepPos q = sweep_pos<G3, true>(p);  // target rows only
   const uint32_t chunk = q.chunk, row = q.row;
-  // target rows past a sequence's own draft count are not read
-  if constexpr (RAGGED) {
-    if (q.j > static_cast<uint32_t>(seq_kb(p, q.seq))) return;
+  // target rows past a sequence's own draft count are not read, nor, in a
+  // later round, those of a sequence whose drafts stopped matching
+  if constexpr (G3) {
+    if (q.level > seq_kb(p, q.seq)) return;
+    if (p.lv0 > 0 && !matched_before(p, q.seq, p.lv0)) return;  // uniform over the wave
   } else if (p.kb) {  // never true as launched; see sweep_pos
     const uint32_t s = row / (p.K + 1u), j = row - s * (p.K + 1u);
     if (j > static_cast<uint32_t>(seq_kb(p, s))) return;
@@ -246,15 +378,15 @@ hipError_t launch_evented(Kern k, const dim3& grid, hipStream_t st, hipEvent_t e
   return hipGetLastError();
 }
 
-// Ragged grids are (chunks, row slots, sequences), at most kMaxGridZ
+// 3-D grids are (chunks, round slots, sequences), at most kMaxGridZ
 // sequences per launch, so larger batches are swept in slices (events, when
-// given, bracket all of them); the others are one-dimensional.
+// given, bracket all of them); the full sweep's grid is one-dimensional.
 constexpr long kMaxGridZ = 65535;
 
 template <typename Kern>
-hipError_t launch_grid(Kern k, bool ragged, unsigned slots, const Params& p, hipStream_t st, hipEvent_t e0,
+hipError_t launch_grid(Kern k, bool g3, unsigned slots, const Params& p, hipStream_t st, hipEvent_t e0,
                        hipEvent_t e1) {
-  if (!ragged)
+  if (!g3)
     return launch_evented(k, dim3(static_cast<unsigned>(static_cast<long>(p.nseq) * slots * p.nch1)), st, e0, e1, p);
   Params q = p;
   for (long s0 = 0; s0 < p.nseq; s0 += kMaxGridZ) {
@@ -267,32 +399,40 @@ hipError_t launch_grid(Kern k, bool ragged, unsigned slots, const Params& p, hip
   return hipSuccess;
 }
 
-template <int DT, bool RAGGED>
-hipError_t launch_lse(const Params& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  const unsigned slots = 2u * static_cast<unsigned>(p.K) + 1u;
-  if (!p.vec) return launch_grid(k_sweep_lse<DT, false, false, RAGGED>, RAGGED, slots, p, st, e0, e1);
-  if (p.sweep_large) return launch_grid(k_sweep_lse<DT, true, true, RAGGED>, RAGGED, slots, p, st, e0, e1);
-  return launch_grid(k_sweep_lse<DT, true, false, RAGGED>, RAGGED, slots, p, st, e0, e1);
+// Round slots: the target rows of levels lv0..lv1-1, then (sampling) the
+// draft rows among them (levels below K); the full sweep: every row.
+inline unsigned sweep_slots(const Params& p, bool argmax) {
+  if (!p.grid3) return argmax ? p.K + 1u : 2u * p.K + 1u;
+  const int drafts = (p.lv1 < p.K ? p.lv1 : p.K) - p.lv0;
+  return static_cast<unsigned>(p.lv1 - p.lv0 + (argmax || drafts < 0 ? 0 : drafts));
 }
 
-template <int DT, bool RAGGED>
+template <int DT, bool G3>
+hipError_t launch_lse(const Params& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const unsigned slots = sweep_slots(p, false);
+  if (!p.vec) return launch_grid(k_sweep_lse<DT, false, false, G3>, G3, slots, p, st, e0, e1);
+  if (p.sweep_large) return launch_grid(k_sweep_lse<DT, true, true, G3>, G3, slots, p, st, e0, e1);
+  return launch_grid(k_sweep_lse<DT, true, false, G3>, G3, slots, p, st, e0, e1);
+}
+
+template <int DT, bool G3>
 hipError_t launch_argmax(const Params& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  const unsigned slots = static_cast<unsigned>(p.K) + 1u;
-  if (!p.vec) return launch_grid(k_sweep_argmax<DT, false, false, RAGGED>, RAGGED, slots, p, st, e0, e1);
-  if (p.sweep_large) return launch_grid(k_sweep_argmax<DT, true, true, RAGGED>, RAGGED, slots, p, st, e0, e1);
-  return launch_grid(k_sweep_argmax<DT, true, false, RAGGED>, RAGGED, slots, p, st, e0, e1);
+  const unsigned slots = sweep_slots(p, true);
+  if (!p.vec) return launch_grid(k_sweep_argmax<DT, false, false, G3>, G3, slots, p, st, e0, e1);
+  if (p.sweep_large) return launch_grid(k_sweep_argmax<DT, true, true, G3>, G3, slots, p, st, e0, e1);
+  return launch_grid(k_sweep_argmax<DT, true, false, G3>, G3, slots, p, st, e0, e1);
 }
 
 hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  const bool ragged = p.kb != nullptr;
-  if (dtype == 1) return ragged ? launch_lse<1, true>(p, st, e0, e1) : launch_lse<1, false>(p, st, e0, e1);
-  return ragged ? launch_lse<0, true>(p, st, e0, e1) : launch_lse<0, false>(p, st, e0, e1);
+  const bool g3 = p.grid3 != 0;
+  if (dtype == 1) return g3 ? launch_lse<1, true>(p, st, e0, e1) : launch_lse<1, false>(p, st, e0, e1);
+  return g3 ? launch_lse<0, true>(p, st, e0, e1) : launch_lse<0, false>(p, st, e0, e1);
 }
 
 hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  const bool ragged = p.kb != nullptr;
-  if (dtype == 1) return ragged ? launch_argmax<1, true>(p, st, e0, e1) : launch_argmax<1, false>(p, st, e0, e1);
-  return ragged ? launch_argmax<0, true>(p, st, e0, e1) : launch_argmax<0, false>(p, st, e0, e1);
+  const bool g3 = p.grid3 != 0;
+  if (dtype == 1) return g3 ? launch_argmax<1, true>(p, st, e0, e1) : launch_argmax<1, false>(p, st, e0, e1);
+  return g3 ? launch_argmax<0, true>(p, st, e0, e1) : launch_argmax<0, false>(p, st, e0, e1);
 }
 
 }  // namespace sv

@@ -60,30 +60,6 @@ constexpr int kRowsPerWave = (kRowsMax + kVWaves - 1) / kVWaves;  // 5 rows per 
 constexpr int kSplitReads = 16;  // reads of the published values before the fp64 fallback
 
 // ------------------------------------------------------------ acceptance --
-// Fold one lane's (R, s) sweep partial into its running pair (ml, sl):
-// exact power-of-two rescales, fp64 sums.
-__device__ inline void fold_partial(float& ml, double& sl, float2 q) {
-  if (q.x == -INFINITY) return;
-  if (q.x > ml) {
-    sl = ml == -INFINITY ? 0.0 : ldexp(sl, static_cast<int>(fmaxf(ml - q.x, -1000.f)));
-    ml = q.x;
-  }
-  sl += ldexp(static_cast<double>(q.y), static_cast<int>(fmaxf(q.x - ml, -1000.f)));
-}
-
-// log2 sum 2^(x c) of a row from the lanes' running pairs (whole wave).  The
-// exponent of the sum is exact (frexp); its mantissa's log2 comes from
-// v_log_f32, good to ~1e-7 absolute, which is all the uses of the normaliser
-// need (the acceptance test's near-tie window is 1e-5 and the draw normalises
-// by its own sums).
-__device__ inline double wave_log2z(float ml, double sl) {
-  const float M = wave_max(ml);
-  const double S = wave_sum(ml == -INFINITY ? 0.0 : ldexp(sl, static_cast<int>(fmaxf(ml - M, -1000.f))));
-  int e;
-  const double m = frexp(S, &e);  // S = m 2^e, m in [1/2, 1)
-  return static_cast<double>(M) + e + __builtin_amdgcn_logf(static_cast<float>(m));
-}
-
 // Runs on the whole workgroup.  When `writer`, writes the accepted prefix and
 // the padding of out_tokens (slot n is the draw's), out_n and out_logz (the
 // other workgroups of a split sequence compute the same record and write

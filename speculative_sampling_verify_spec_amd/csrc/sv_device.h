@@ -214,6 +214,33 @@ __device__ inline void wave_argmax(float& v, int& i) {
   i = __builtin_amdgcn_readlane(i, 63);
 }
 
+// ------------------------------------------------------ sweep partials --
+// Fold one lane's (R, s) sweep partial into its running pair (ml, sl):
+// exact power-of-two rescales, fp64 sums.  Any float pair is safe here (the
+// shift counts are clamped to [-1000, 0]), so stale partials of rows a call
+// did not sweep give meaningless but harmless values.
+__device__ inline void fold_partial(float& ml, double& sl, float2 q) {
+  if (q.x == -INFINITY) return;
+  if (q.x > ml) {
+    sl = ml == -INFINITY ? 0.0 : ldexp(sl, static_cast<int>(fmaxf(ml - q.x, -1000.f)));
+    ml = q.x;
+  }
+  sl += ldexp(static_cast<double>(q.y), static_cast<int>(fmaxf(q.x - ml, -1000.f)));
+}
+
+// log2 sum 2^(x c) of a row from the lanes' running pairs (whole wave).  The
+// exponent of the sum is exact (frexp); its mantissa's log2 comes from
+// v_log_f32, good to ~1e-7 absolute, which is all the uses of the normaliser
+// need (the acceptance test's near-tie window is 1e-5 and the draw normalises
+// by its own sums).
+__device__ inline double wave_log2z(float ml, double sl) {
+  const float M = wave_max(ml);
+  const double S = wave_sum(ml == -INFINITY ? 0.0 : ldexp(sl, static_cast<int>(fmaxf(ml - M, -1000.f))));
+  int e;
+  const double m = frexp(S, &e);  // S = m 2^e, m in [1/2, 1)
+  return static_cast<double>(M) + e + __builtin_amdgcn_logf(static_cast<float>(m));
+}
+
 // Workgroup-wide sum of one double per thread over NW waves; every thread
 // gets the total.
 template <int NW>

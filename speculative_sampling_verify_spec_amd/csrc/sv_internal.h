@@ -25,6 +25,18 @@ constexpr int kSweepElems() {
 }
 constexpr long kSweepLargeMinGroups = 6144;
 
+// Early exit.  Acceptance stops at a sequence's first rejection n, and only
+// the rows of levels 0..n are needed (level k < K_b: target row k and draft
+// row k; level K_b: the bonus target row).  The sweep therefore runs in
+// rounds over levels [lv0, lv1): [0, 1), [1, 3), [3, K + 1).  A workgroup of
+// a later round first repeats the acceptance tests of levels 0..lv0-1 from
+// the partials the earlier rounds wrote, and leaves without loading its
+// chunk when the sequence has already rejected.  The repeated tests fold at
+// most kMaxProLevels levels.
+constexpr int kMaxProLevels = 3;
+constexpr int kMaxRounds = 3;
+__host__ __device__ constexpr int round_begin(int r) { return r == 0 ? 0 : (r == 1 ? 1 : 3); }
+
 // The fast draw (k_verify) streams a sequence's decisive row(s) in wave
 // iterations of 64 lanes x kDrawLaneUnits units (16-byte vectors, or single
 // elements on the scalar path), grouped into at most kMaxSegs segments of
@@ -125,6 +137,10 @@ struct Params {
   int nch1, ch1;             // sweep chunks per row, elements per sweep chunk (at most)
   int cq, cr;                // sweep chunk c spans c*cq + min(c, cr) .. + cq + (c < cr) units
   int sweep_large;           // the sweep runs its large shape (see kSweepElems)
+  int grid3;                 // the sweep's grid: 0 one-dimensional over every row; 1 (chunks, round
+                             // slots, sequences) over the rows of levels lv0..lv1-1 each sequence uses
+  int lv0, lv1;              // grid3: the levels the launch covers (target rows lv0..lv1-1, and the
+                             // draft rows among them); lv0 > 0: re-test levels 0..lv0-1 first
   int R3, ch3;               // fp64 draw chunks per row, elements per chunk
   int seq0, nseq;            // the sequences a launch covers
   int split;                 // workgroups per sequence in k_verify (1: no split)
