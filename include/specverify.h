@@ -98,6 +98,15 @@ size_t spec_verify_workspace_size(int B, int K, int V, int dtype, float T);
  * Outputs: out_tokens[b] = x_0..x_{n-1}, the drawn token, then -1 padding;
  * out_n_accepted[b] = n in [0, K] ([B] "多 Token 验证": one to k+1 tokens).
  *
+ * Rows past a sequence's first rejection are never needed.  When the logit
+ * rows total at least 256 MiB (B*(2K+1)*V*element_size; B*(K+1)*V*... in
+ * greedy mode), the rows are read in rounds of positions 0, 1-2 and 3-K, and
+ * a round skips the sequences that rejected in an earlier one; smaller
+ * inputs are read in one sweep.  The environment variable
+ * SPECV_ROUNDS_MIN_BYTES, read once per process, replaces that threshold (0:
+ * always rounds).  Both ways give identical outputs.  spec_verify_ex and
+ * spec_verify_ragged_ex with out_logz always read every row.
+ *
  * logits_p      [B][K+1][V] target logits (dtype)
  * logits_q      [B][K][V]   draft logits (dtype); may be NULL iff T == 0
  * draft_tokens  [B][K] int32

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <limits>
 #include <mutex>
 
@@ -56,6 +57,8 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
   size_t off = 0;
   L.part = off;
   off = align_up(off + static_cast<size_t>(rows) * L.nch1 * kWaves * sizeof(float2));
+  L.kbs = off;
+  off = align_up(off + static_cast<size_t>(B) * sizeof(int32_t));
   if (greedy) {
     L.total = off;
     return L;
@@ -133,9 +136,25 @@ int verify_split(int B, int V, int dtype, bool vec) {
   return std::max(1, std::min(std::min(cus / B, blocks), kMaxSplit));
 }
 
-// The sweep's launches for one call: every row at once when `full` (the
-// caller asked for every row's normaliser), else rounds of levels (see
-// kMaxProLevels), each launch's events given to the first and last.
+// Bytes of logit rows from which the sweep runs in rounds: kRoundsMinBytes,
+// or SPECV_ROUNDS_MIN_BYTES from the environment (read once per process).
+double rounds_min_bytes() {
+  static std::once_flag once;
+  static double v = kRoundsMinBytes;
+  std::call_once(once, [] {
+    const char* e = std::getenv("SPECV_ROUNDS_MIN_BYTES");
+    if (e && *e) {
+      char* end = nullptr;
+      const double d = std::strtod(e, &end);
+      if (end != e && d >= 0.0) v = d;
+    }
+  });
+  return v;
+}
+
+// The sweep's launches for one call: every row at once when `full`, else
+// rounds of levels (see round_begin) with k_round_accept between them; the
+// events go to the first and the last sweep launch.
 hipError_t launch_sweeps(Params P, int dtype, bool greedy, bool full, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   auto launch = [&](const Params& q, hipEvent_t a, hipEvent_t b) {
     return greedy ? launch_sweep_argmax(q, dtype, st, a, b) : launch_sweep_lse(q, dtype, st, a, b);
@@ -151,6 +170,13 @@ hipError_t launch_sweeps(Params P, int dtype, bool greedy, bool full, hipStream_
   bounds[nr] = P.K + 1;
   P.grid3 = 1;
   for (int r = 0; r < nr; ++r) {
+    if (r > 0) {  // the tests of the round just swept
+      Params A = P;
+      A.lv0 = bounds[r - 1];
+      A.lv1 = bounds[r];
+      const hipError_t rc = launch_round_accept(A, dtype, greedy, st);
+      if (rc != hipSuccess) return rc;
+    }
     P.lv0 = bounds[r];
     P.lv1 = bounds[r + 1];
     const hipError_t rc = launch(P, r == 0 ? e0 : nullptr, r == nr - 1 ? e1 : nullptr);
@@ -245,8 +271,11 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   hipEvent_t e0 = static_cast<hipEvent_t>(ev_sweep_begin), e1 = static_cast<hipEvent_t>(ev_sweep_end);
   const bool timed = e0 && e1;
 
-  // every row's normaliser asked for: one sweep of every row; else rounds
-  const bool full = out_logz != nullptr;
+  // one sweep of every row when every row's normaliser is asked for or the
+  // input is small; else rounds
+  const long all_rows = static_cast<long>(B) * (greedy ? K + 1 : 2 * K + 1);
+  const bool full = out_logz != nullptr || static_cast<double>(all_rows) * V * eb < rounds_min_bytes();
+  P.kbs = reinterpret_cast<int32_t*>(ws + L.kbs);
   if (greedy) {
     if (launch_sweeps(P, dtype, true, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
       return SPECV_E_HIP;

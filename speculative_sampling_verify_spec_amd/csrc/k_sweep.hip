@@ -18,16 +18,14 @@
 // workgroup each, so no workgroup gets a short tail; each wave writes its own
 // partial, so no workgroup barrier holds finished waves back.
 //
-// Rounds.  Without a request for every row's normaliser, the sweep runs in
-// rounds of levels (see kMaxProLevels): acceptance stops at the first
-// rejection ([B] "多 Token 验证：左到右，遇错即停"), so rows past it are never
-// needed.  A round's grid is (chunks, round slots, sequences); a workgroup of
-// a later round first repeats, in every wave for itself, the acceptance
-// tests of the earlier levels from the partials already written (the same
-// fold and test as the acceptance scan after the sweep), and leaves before
-// loading anything when its sequence has rejected.  Rows of levels past a
-// rejection keep stale partials, which only ever decide tests after the
-// first failing one.
+// Rounds.  On large inputs, unless every row's normaliser is asked for, the
+// sweep runs in rounds of levels (see round_begin): acceptance stops at the
+// first rejection ([B] "多 Token 验证：左到右，遇错即停"), so rows past it are
+// never needed.  A round's grid is (chunks, round slots, sequences); between
+// rounds k_round_accept tests the levels just swept and lowers a rejected
+// sequence's last level to sweep, which the next round's workgroups compare
+// with one scalar load before leaving.  Rows of levels past a rejection keep
+// stale partials, which only ever decide tests after the first failing one.
 #include <hip/hip_ext.h>
 
 #include "sv_device.h"
@@ -96,113 +94,6 @@ __device__ inline SweepPos sweep_pos(const Params& p) {
     q.draft = false;
   }
   return q;
-}
-
-// ------------------------------------------------ the earlier levels' tests --
-// Partials of row j of sequence s, lanes lane and lane + 64, loaded
-// branch-free (clamped index, masked afterwards) so that every row's loads
-// are in flight together.
-__device__ inline void load_row_partials(const Params& p, long s, uint32_t per_seq, int j, bool in, int np,
-                                         float2 (&q)[2], float2 empty) {
-  const int lane = threadIdx.x % kWave;
-  const float2* base = p.part + (s * per_seq + (in ? j : 0)) * np;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int i = lane + h * kWave;
-    const float2 v = base[i < np ? i : np - 1];
-    q[h] = (in && i < np) ? v : empty;
-  }
-}
-
-// Whether sequence s accepted its drafts at levels 0..a-1 (1 <= a <=
-// kMaxProLevels, a <= K_b), from the sweep partials of those levels' target
-// and draft rows: the acceptance scan's fold and test.  Whole wave.
-template <int DT>
-__device__ inline bool accepted_before(const Params& p, long s, int a) {
-  const int lane = threadIdx.x % kWave;
-  const int K = p.K, np = p.nch1 * kWaves;
-  const uint32_t per_seq = 2u * K + 1u;
-  // the partials of the 2a rows go out first, then draft token -> its logits
-  float2 q[2 * kMaxProLevels][2];
-#pragma unroll
-  for (int r = 0; r < kMaxProLevels; ++r) {
-    load_row_partials(p, s, per_seq, r, r < a, np, q[r], make_float2(-INFINITY, 0.f));
-    load_row_partials(p, s, per_seq, K + 1 + r, r < a, np, q[kMaxProLevels + r], make_float2(-INFINITY, 0.f));
-  }
-  const int li = lane < a ? lane : 0;
-  const int xk = p.x[s * K + li];
-  const float u = p.ua[s * K + li];
-  const bool valid = xk >= 0 && xk < p.V;
-  const int xs = valid ? xk : 0;
-  const float xp = Elt<DT>::at(row_ptr<DT>(p.lp, s * (K + 1) + li, p.V), xs);
-  const float xq = Elt<DT>::at(row_ptr<DT>(p.lq, s * K + li, p.V), xs);
-  float ml[2 * kMaxProLevels];
-  double sl[2 * kMaxProLevels];
-#pragma unroll
-  for (int r = 0; r < 2 * kMaxProLevels; ++r) {
-    ml[r] = -INFINITY;
-    sl[r] = 0.0;
-    fold_partial(ml[r], sl[r], q[r][0]);
-    fold_partial(ml[r], sl[r], q[r][1]);
-  }
-  for (int i = lane + 2 * kWave; i < np; i += kWave)  // long rows: the rest of the partials
-#pragma unroll
-    for (int r = 0; r < kMaxProLevels; ++r) {
-      if (r < a) {
-        fold_partial(ml[r], sl[r], p.part[(s * per_seq + r) * np + i]);
-        fold_partial(ml[kMaxProLevels + r], sl[kMaxProLevels + r], p.part[(s * per_seq + K + 1 + r) * np + i]);
-      }
-    }
-  double lzp = 0.0, lzq = 0.0;  // lane k: log2 Z of target row k and of draft row k
-#pragma unroll
-  for (int r = 0; r < kMaxProLevels; ++r) {
-    if (r < a) {  // uniform over the wave
-      const double zp = wave_log2z(ml[r], sl[r]);
-      const double zq = wave_log2z(ml[kMaxProLevels + r], sl[kMaxProLevels + r]);
-      if (lane == r) {
-        lzp = zp;
-        lzq = zq;
-      }
-    }
-  }
-  bool accept = false;
-  if (lane < a && valid) {
-    const double c = p.c;
-    const double lr = (static_cast<double>(xp) * c - lzp) - (static_cast<double>(xq) * c - lzq);
-    const double thr = lr >= 0.0 ? 1.0 : exp2(lr);
-    accept = static_cast<double>(u) < thr;
-  }
-  return __ballot(lane < a && !accept) == 0;
-}
-
-// Greedy: whether the drafts at levels 0..a-1 equal the first arg-max of
-// their target rows, from the arg-max sweep's partials.  Whole wave.
-__device__ inline bool matched_before(const Params& p, long s, int a) {
-  const int lane = threadIdx.x % kWave;
-  const int K = p.K, np = p.nch1 * kWaves;
-  const uint32_t per_seq = K + 1u;
-  float2 q[kMaxProLevels][2];
-#pragma unroll
-  for (int r = 0; r < kMaxProLevels; ++r)
-    load_row_partials(p, s, per_seq, r, r < a, np, q[r], make_float2(-INFINITY, __int_as_float(0x7fffffff)));
-  const int xk = p.x[s * K + (lane < a ? lane : 0)];
-  int am = -1;  // lane k: the arg-max of target row k
-#pragma unroll
-  for (int r = 0; r < kMaxProLevels; ++r) {
-    if (r < a) {  // uniform over the wave
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      argmax_merge(bv, bi, q[r][0].x, __float_as_int(q[r][0].y));
-      argmax_merge(bv, bi, q[r][1].x, __float_as_int(q[r][1].y));
-      for (int i = lane + 2 * kWave; i < np; i += kWave) {
-        const float2 v = p.part[(s * per_seq + r) * np + i];
-        argmax_merge(bv, bi, v.x, __float_as_int(v.y));
-      }
-      wave_argmax(bv, bi);
-      if (lane == r) am = bi;
-    }
-  }
-  return __ballot(lane < a && xk != am) == 0;
 }
 
 // Block 0 of a launch (both grid shapes).
@@ -281,9 +172,8 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   // kernel keeps the order it was tuned with: reset first, then a test of
   // the counts, which is never true as launched.
   if constexpr (G3) {
-    const int kb = seq_kb(p, q.seq);
+    const int kb = sweep_kb(p, q.seq);
     if (q.draft ? q.level >= kb : q.level > kb) return;
-    if (p.lv0 > 0 && !accepted_before<DT>(p, q.seq, p.lv0)) return;  // uniform over the wave
   } else {
     if (first_block()) reset_state(p);
     if (p.kb) {
@@ -338,8 +228,7 @@ __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
   // target rows past a sequence's own draft count are not read, nor, in a
   // later round, those of a sequence whose drafts stopped matching
   if constexpr (G3) {
-    if (q.level > seq_kb(p, q.seq)) return;
-    if (p.lv0 > 0 && !matched_before(p, q.seq, p.lv0)) return;  // uniform over the wave
+    if (q.level > sweep_kb(p, q.seq)) return;
   } else if (p.kb) {  // never true as launched; see sweep_pos
     const uint32_t s = row / (p.K + 1u), j = row - s * (p.K + 1u);
     if (j > static_cast<uint32_t>(seq_kb(p, s))) return;

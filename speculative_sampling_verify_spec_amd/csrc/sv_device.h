@@ -43,6 +43,13 @@ __device__ inline int seq_kb(const Params& p, long s) {
   return p.kb ? min(max(p.kb[s], 0), p.K) : p.K;
 }
 
+// The last level the sweep reads for sequence s: its draft count, or, in a
+// round after the first, the level of its first rejection once it has
+// rejected (written by k_round_accept).
+__device__ inline int sweep_kb(const Params& p, long s) {
+  return p.lv0 > 0 ? p.kbs[s] : seq_kb(p, s);
+}
+
 template <int DT>
 __device__ inline const void* row_ptr(const void* base, long row, int V) {
   return static_cast<const char*>(base) + row * static_cast<long>(V) * Elt<DT>::kBytes;

@@ -27,15 +27,18 @@ constexpr long kSweepLargeMinGroups = 6144;
 
 // Early exit.  Acceptance stops at a sequence's first rejection n, and only
 // the rows of levels 0..n are needed (level k < K_b: target row k and draft
-// row k; level K_b: the bonus target row).  The sweep therefore runs in
-// rounds over levels [lv0, lv1): [0, 1), [1, 3), [3, K + 1).  A workgroup of
-// a later round first repeats the acceptance tests of levels 0..lv0-1 from
-// the partials the earlier rounds wrote, and leaves without loading its
-// chunk when the sequence has already rejected.  The repeated tests fold at
-// most kMaxProLevels levels.
-constexpr int kMaxProLevels = 3;
+// row k; level K_b: the bonus target row).  On inputs of at least
+// kRoundsMinBytes the sweep therefore runs in rounds over levels [lv0, lv1):
+// [0, 1), [1, 3), [3, K + 1).  After each round but the last,
+// k_round_accept tests the levels it swept (at most kMaxRoundLevels) and
+// writes each sequence's last level still to sweep; the next round's
+// workgroups of a sequence that has rejected leave at once.  Smaller inputs
+// take one sweep of every row: there the extra launches cost more than the
+// rows they save.
 constexpr int kMaxRounds = 3;
+constexpr int kMaxRoundLevels = 2;  // levels of a round that another round follows
 __host__ __device__ constexpr int round_begin(int r) { return r == 0 ? 0 : (r == 1 ? 1 : 3); }
+constexpr double kRoundsMinBytes = 256.0 * (1 << 20);
 
 // The fast draw (k_verify) streams a sequence's decisive row(s) in wave
 // iterations of 64 lanes x kDrawLaneUnits units (16-byte vectors, or single
@@ -140,7 +143,8 @@ struct Params {
   int grid3;                 // the sweep's grid: 0 one-dimensional over every row; 1 (chunks, round
                              // slots, sequences) over the rows of levels lv0..lv1-1 each sequence uses
   int lv0, lv1;              // grid3: the levels the launch covers (target rows lv0..lv1-1, and the
-                             // draft rows among them); lv0 > 0: re-test levels 0..lv0-1 first
+                             // draft rows among them); lv0 > 0: skip the rows past kbs[s]
+  int32_t* kbs;              // [B] rounds: the last level still to sweep per sequence (k_round_accept)
   int R3, ch3;               // fp64 draw chunks per row, elements per chunk
   int seq0, nseq;            // the sequences a launch covers
   int split;                 // workgroups per sequence in k_verify (1: no split)
@@ -152,7 +156,7 @@ struct Params {
 
 // Workspace layout (byte offsets), shared by spec_verify_workspace_size and the launcher.
 struct Layout {
-  size_t part, xsum, queue, qcount, segm, spq, vcount, total;
+  size_t part, kbs, xsum, queue, qcount, segm, spq, vcount, total;
   int nch1, ch1, cq, cr, R3, ch3;
   int sweep_large;  // the sweep's large shape (see kSweepElems)
 };
@@ -165,6 +169,7 @@ hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t s, hipEve
 hipError_t launch_verify(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_exact(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_greedy_scan(const Params& p, hipStream_t s);
+hipError_t launch_round_accept(const Params& p, int dtype, bool greedy, hipStream_t s);
 hipError_t launch_position_stats(const Params& p, hipStream_t s);
 hipError_t launch_tree_scan(const Params& p, hipStream_t s);
 hipError_t launch_ngram(const int32_t* hist, const int32_t* lengths, int B, int Lmax, int n_min, int n_max,
