@@ -29,7 +29,7 @@ int elt_bytes(int dtype) { return dtype == SPECV_BF16 ? 2 : 4; }
 
 }  // namespace
 
-Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
+Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy, bool tree) {
   Layout L{};
   // sweep chunks: equal shares of a row, each at most one workgroup's worth
   const int per_vec = vec ? (dtype == SPECV_BF16 ? 8 : 4) : 1;
@@ -47,8 +47,16 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy) {
     const long units_per_chunk = static_cast<long>(kBlock) * (lane_elems / per_vec);
     return units > 0 ? (units + units_per_chunk - 1) / units_per_chunk : 1L;
   };
-  // the large shape when it still gives the launch enough workgroups
-  L.sweep_large = vec && rows * chunks(elems(true)) >= kSweepLargeMinGroups ? 1 : 0;
+  // the large shape when it still gives a launch enough workgroups, judged on
+  // the whole sweep for token trees, else on the first round of the
+  // early-exit sweep (position 0 of every sequence):
+  // the better rule for rounds (headline: 138.6 against 143.1 us per step
+  // with the small shape; the sharp fp32 workload, whose first round alone
+  // has 36864 large-shape workgroups: 727 against 766 us with the large
+  // one).  The one-sweep path takes the same shape, so that both compute
+  // bit-identical partials and hence identical outputs.
+  const long launch_rows = tree ? rows : static_cast<long>(B) * (greedy ? 1 : 2);
+  L.sweep_large = vec && launch_rows * chunks(elems(true)) >= kSweepLargeMinGroups ? 1 : 0;
   const int lane_elems = elems(L.sweep_large != 0);
   L.ch1 = kBlock * lane_elems;  // elements per chunk, at most
   L.nch1 = static_cast<int>(chunks(lane_elems));
@@ -212,8 +220,8 @@ size_t spec_verify_workspace_size(int B, int K, int V, int dtype, float T) {
   if (!sv::valid_temperature(T)) return 0;
   const bool greedy = T == 0.f;
   if (!sv::valid_shape(B, K, V, greedy)) return 0;
-  const size_t a = sv::make_layout(B, K, V, dtype, false, greedy).total;
-  const size_t b = sv::make_layout(B, K, V, dtype, true, greedy).total;
+  const size_t a = sv::make_layout(B, K, V, dtype, false, greedy, false).total;
+  const size_t b = sv::make_layout(B, K, V, dtype, true, greedy, false).total;
   return a > b ? a : b;
 }
 
@@ -237,7 +245,11 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   const uintptr_t aq = greedy ? 0 : reinterpret_cast<uintptr_t>(logits_q);
   if (ap % eb || aq % eb) return SPECV_E_ALIGN;
   const bool vec = ap % 16 == 0 && aq % 16 == 0 && (static_cast<long>(V) * eb) % 16 == 0;
-  const Layout L = make_layout(B, K, V, dtype, vec, greedy);
+  // one sweep of every row when every row's normaliser is asked for or the
+  // input is small; else rounds
+  const long all_rows = static_cast<long>(B) * (greedy ? K + 1 : 2 * K + 1);
+  const bool full = out_logz != nullptr || static_cast<double>(all_rows) * V * eb < rounds_min_bytes();
+  const Layout L = make_layout(B, K, V, dtype, vec, greedy, false);
   if (need) *need = L.total;
   if (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign || workspace_bytes < L.total)
     return SPECV_E_WORKSPACE;
@@ -271,10 +283,6 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   hipEvent_t e0 = static_cast<hipEvent_t>(ev_sweep_begin), e1 = static_cast<hipEvent_t>(ev_sweep_end);
   const bool timed = e0 && e1;
 
-  // one sweep of every row when every row's normaliser is asked for or the
-  // input is small; else rounds
-  const long all_rows = static_cast<long>(B) * (greedy ? K + 1 : 2 * K + 1);
-  const bool full = out_logz != nullptr || static_cast<double>(all_rows) * V * eb < rounds_min_bytes();
   P.kbs = reinterpret_cast<int32_t*>(ws + L.kbs);
   if (greedy) {
     if (launch_sweeps(P, dtype, true, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
@@ -379,8 +387,8 @@ bool valid_tree_shape(int B, int N, int V) {
 }
 
 size_t tree_workspace(int B, int N, int V, int dtype) {
-  const size_t a = make_layout(B, N - 1, V, dtype, false, true).total;
-  const size_t b = make_layout(B, N - 1, V, dtype, true, true).total;
+  const size_t a = make_layout(B, N - 1, V, dtype, false, true, true).total;
+  const size_t b = make_layout(B, N - 1, V, dtype, true, true, true).total;
   return a > b ? a : b;
 }
 
@@ -404,7 +412,7 @@ int spec_verify_tree_greedy(const void* logits, const int32_t* tree_tokens, cons
   const uintptr_t ap = reinterpret_cast<uintptr_t>(logits);
   if (ap % eb) return SPECV_E_ALIGN;
   const bool vec = ap % 16 == 0 && (static_cast<long>(V) * eb) % 16 == 0;
-  const Layout L = make_layout(B, N - 1, V, dtype, vec, true);
+  const Layout L = make_layout(B, N - 1, V, dtype, vec, true, true);
   if (!workspace || reinterpret_cast<uintptr_t>(workspace) % kAlign || workspace_bytes < L.total)
     return SPECV_E_WORKSPACE;
   Params P{};

@@ -161,7 +161,7 @@ struct Layout {
   int sweep_large;  // the sweep's large shape (see kSweepElems)
 };
 
-Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy);
+Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy, bool tree);
 
 // Launchers (one per kernel), defined next to their kernels.
 hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
