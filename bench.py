@@ -58,10 +58,11 @@ HEADLINE = 2
 # The library's sweep rounds (levels [0, 1), [1, 3), [3, K + 1)) unless every
 # row's log Z is asked for; used here only to count the bytes a step reads.
 ROUND_BEGINS = (0, 1, 3)
-COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "sweep_lse_headline_counters.md")
-# the sweep kernel's source: its file and the headers it includes (hashed in this order)
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "sweep_headline_counters.md")
+# the sweep phase's sources: its kernels, the headers they include and the
+# host code that sets their launch shapes (hashed in this order)
 SWEEP_SOURCES = [os.path.join(ROOT, "speculative_sampling_verify_spec_amd", "csrc", f)
-                 for f in ("k_sweep.hip", "sv_device.h", "sv_internal.h")]
+                 for f in ("k_sweep.hip", "k_rounds.hip", "sv_device.h", "sv_internal.h", "api.cpp")]
 
 
 def sweep_source_sha256() -> str:
@@ -101,8 +102,9 @@ class HipEvents:
 
 
 def counter_traffic(swept_bytes: int):
-    """HBM bytes per sweep launch from the committed rocprofv3 counter summary,
-    or None when it is missing or was taken on a different sweep kernel."""
+    """HBM bytes of the sweep phase per step from the committed rocprofv3
+    counter summary, or None when it is missing or was taken on different
+    sweep kernels."""
     if not os.path.exists(COUNTER_SUMMARY):
         return None
     text = open(COUNTER_SUMMARY).read()
@@ -482,14 +484,23 @@ def main():
     else:
         sweep_s = float(np.mean(sweep_ms)) / 1e3
         achieved = swept / sweep_s / 1e9
-        line["roofline"] = {"bound": "hbm", "kernel": "sweep_lse" if not greedy else "sweep_argmax",
+        full = args.full or (swept_all * 1.0 < 256 * 2 ** 20)  # the library's rounds threshold (default)
+        nr = 1 if full else len([b for b in ROUND_BEGINS if b <= K])
+        kname = "k_sweep_lse" if not greedy else "k_sweep_argmax"
+        line["roofline"] = {"bound": "hbm",
+                            "kernel": f"row sweep: {kname}" if nr == 1 else
+                                      f"row sweep: {nr} round launches of {kname} and {nr - 1} of k_round_accept "
+                                      "between them, timed together (first sweep dispatch start to last end)",
                             "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": achieved / PEAK_HBM_GBS,
-                            # the committed counters cover the log-sum-exp sweep only
-                            "traffic": None if greedy else counter_traffic(swept),
+                            # the committed counters cover the headline's log-sum-exp sweep
+                            "traffic": None if (greedy or args.full or args.seqs or args.workload != HEADLINE)
+                            else counter_traffic(swept),
                             "launch_us": sweep_s * 1e6, "launches_timed": args.steps,
-                            "sweep_launches_per_step": 1 if args.full else len([b for b in ROUND_BEGINS if b <= K]),
-                            "algorithmic_bytes_per_launch": swept}
+                            "sweep_launches_per_step": nr,
+                            "algorithmic_bytes_per_launch": swept,
+                            "algorithmic_bytes": "the logit rows the sweep reads (rows of the positions each "
+                                                 "sequence reached), V * element size each"}
     if not args.no_cpu_baseline:
         log(f"timing the fp64 oracle on a sample (~{args.cpu_seconds:.0f}s)")
         line["cpu_baseline"] = cpu_baseline(batch, tok_host, n_host, args.cpu_seconds)
