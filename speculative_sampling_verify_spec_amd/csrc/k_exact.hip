@@ -7,7 +7,8 @@
 // w = max(0, P - rho Q) / sum P with rho = sum P / sum Q.
 //
 // Two kernels walk the queue the fast draw filled (each entry is the
-// sequence's whole record, read together with the queue's length):
+// sequence's whole record, read together with the queue's length); rows of
+// at most two chunks take one kernel that does both (k_exact_solo):
 //   exact_chunks (queued sequences x chunks of ch3 >= 1024 tokens): per chunk
 //        sum P, sum Q, A = sum max(0, P - Q), G = sum_{P > Q} Q and
 //        H = sum_{near flip} Q, the Q-mass within a relative kKappa of P = Q.
@@ -37,6 +38,8 @@ constexpr int kRun = 8;                          // elements per lane per rescan
 constexpr int kRound = kXBlock * kRun;           // 1024 elements per round (the smallest chunk)
 constexpr double kKappa = 1e-4;                  // near-flip window, relative to Q
 constexpr unsigned kExactSeqs = 32;              // queued sequences the kernels cover per pass
+constexpr int kSoloMaxChunks = 2;                // rows of at most this many chunks: one launch (k_exact_solo)
+constexpr unsigned kSoloSeqs = 256;              // queued sequences k_exact_solo covers per pass
 constexpr int kMaxPer = (kMaxDrawChunks + kWave - 1) / kWave;  // chunks per lane in the select
 
 // fp64 weight exp(x / T - L'), L' the natural-log reference.
@@ -443,10 +446,53 @@ __global__ __launch_bounds__(kXBlock) void k_exact_select(Params p) {
   }
 }
 
+// Rows of at most kSoloMaxChunks chunks (V <= 2048): one workgroup per
+// queued sequence computes every chunk's sums itself, into LDS, and makes
+// the draw, so the fp64 draw takes one launch (its fixed cost is most of a
+// call on such small rows).  The sums and the draw are those of the two
+// kernels above.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kXBlock) void k_exact_solo(Params p) {
+  const SeqRec first = entry_ahead(p, blockIdx.x);
+  const long count = static_cast<long>(p.qcount[0]);
+  __shared__ double s_cs[kSoloMaxChunks][5];
+  const int lane = threadIdx.x % kWave, per = (p.R3 + kWave - 1) / kWave;
+  for (long e = blockIdx.x; (e < count) & (first.seq >= 0); e += gridDim.x) {
+    SeqRec rec = first;
+    if (e != blockIdx.x) rec = p.queue[p.seq0 + e];
+    const long s = rec.seq;
+    const bool bonus = rec.n == rec.kb;
+    const Rows<DT> rows = decisive_rows<DT>(p, s, rec);
+    const ExactWeight wt = exact_weight(p, rec);
+    __syncthreads();  // the previous entry's reads of s_cs are done
+    for (int r = 0; r < p.R3; ++r) exact_chunk_sums<DT, VEC>(p, rows, wt, bonus, r, s_cs[r]);
+    __syncthreads();
+    ChunkSums cv;  // as load_chunk_sums lays them out (a bonus draw has sum P only)
+#pragma unroll
+    for (int k = 0; k < kMaxPer; ++k) {
+      const int c = lane * per + k;
+      const bool in = threadIdx.x < kWave && k < per && c < p.R3;
+#pragma unroll
+      for (int f = 0; f < 5; ++f) cv.v[k][f] = (in && (f == 0 || !bonus)) ? s_cs[in ? c : 0][f] : 0.0;
+    }
+    int token;
+    bool zw_zero;
+    select_exact<DT, VEC>(p, rows, wt, bonus, cv, static_cast<double>(p.ur[s]), &token, &zw_zero);
+    if (threadIdx.x == 0) {
+      p.out_tokens[s * (p.K + 1) + rec.n] = token;
+      if (p.out_flags && zw_zero) p.out_flags[s] |= SPECV_FLAG_ZW_ZERO;
+    }
+  }
+}
+
 template <int DT, bool VEC>
 void launch_all(const Params& p, hipStream_t st) {
   const dim3 block(kXBlock);
   const unsigned ns = static_cast<unsigned>(p.nseq);
+  if (p.R3 <= kSoloMaxChunks) {
+    hipLaunchKernelGGL((k_exact_solo<DT, VEC>), dim3(ns < kSoloSeqs ? ns : kSoloSeqs), block, 0, st, p);
+    return;
+  }
   // grids cover up to kExactSeqs queued sequences in one pass; idle
   // workgroups exit at once
   const unsigned nx = ns < kExactSeqs ? ns : kExactSeqs;

@@ -46,10 +46,15 @@ def edge_uniforms(b, ref, lo_min=1e-3, margin_lo=1e-11, margin_hi=1e-7):
     return ur, np.array(chosen, dtype=np.int64), np.array(tokens, dtype=np.int64)
 
 
-@pytest.mark.parametrize("cfg,nseq", [(1, None), (2, 32), (3, 16)], ids=["small-bf16", "headline-bf16", "sharp-fp32"])
-def test_draws_at_an_edge_go_to_fp64_and_match(gpu_lib, cfg, nseq):
+# V = 999, 1000 and 2000: rows of one and two fp64 chunks, drawn by the
+# one-launch kernel (V = 999: element loads, not 16-byte vectors)
+@pytest.mark.parametrize("cfg,nseq,V", [(1, None, None), (2, 32, None), (3, 16, None), (1, 48, 1000), (0, 40, 2000),
+                                        (1, 24, 999)],
+                         ids=["small-bf16", "headline-bf16", "sharp-fp32", "V1000-bf16", "V2000-fp32",
+                              "V999-bf16-scalar"])
+def test_draws_at_an_edge_go_to_fp64_and_match(gpu_lib, cfg, nseq, V):
     seqs = None if nseq is None else range(nseq)
-    b = workloads.make_batch(cfg, seqs=seqs, workers=workloads.default_workers())
+    b = workloads.make_batch(cfg, seqs=seqs, workers=workloads.default_workers(), V=V)
     ref = oracle.verify_batch(b)
     ur, chosen, tokens = edge_uniforms(b, ref)
     print(f"cfg {cfg}: {len(chosen)} of {b.B} sequences get an edge uniform", flush=True)
