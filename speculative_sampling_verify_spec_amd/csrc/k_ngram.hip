@@ -7,7 +7,9 @@
 // (1 <= e <= L - 1, so a token follows it) where h[e-n..e) == h[L-n..L).
 // Ends are visited in rounds of 4096, sixteen per thread; a round's tokens and
 // the 16 before them are staged in LDS from registers filled by coalesced
-// loads.  The loads of the first four rounds (histories up to 16385 tokens)
+// loads: 16-byte vectors of four consecutive tokens per lane when the rows
+// allow it (L_max a multiple of 4, an aligned history), which measured far
+// faster than one token per lane, else single tokens.  The loads of the first four rounds (histories up to 16385 tokens)
 // all go out before the first round, so that rounds do not wait for memory
 // one after another; longer histories load their later rounds one at a time.
 // Each thread first compares the last token of its ends with the suffix's
@@ -31,7 +33,15 @@ constexpr int kNgPer = 16;                       // ends per thread per round
 constexpr int kNgRound = kNgBlock * kNgPer;
 constexpr int kNgPre = 4;                        // rounds loaded before the first (histories up to 16385 tokens)
 
-template <int NM>
+// Offset within a round of thread t's r-th token (and end): VEC4, the four
+// tokens of vector r / 4 (vectors of a round 1024 tokens apart); otherwise
+// every 256th token.  Both increase with r.
+template <bool VEC4>
+__device__ inline int ng_off(int r, int t) {
+  return VEC4 ? (r >> 2) * (kNgBlock * 4) + 4 * t + (r & 3) : r * kNgBlock + t;
+}
+
+template <int NM, bool VEC4>
 __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const int32_t* lengths, int Lmax,
                                                     int n_min, int n_max, int min_hits, int K,
                                                     int32_t* out_draft, int32_t* out_count) {
@@ -51,9 +61,27 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
   //    counted apart from the vector loads (waiting for it does not wait for
   //    the tokens);
   //  - the tokens of rounds 1 .. kNgPre - 1, clamped to the last token.
-  int32_t v[kNgPre][kNgPer], hv[kNgPre];  // round pr's tokens h[pr * kNgRound + r * kNgBlock + t], and the NM before it
+  // round pr's tokens h[pr * kNgRound + ng_off(r, t)], and the NM before it.
+  // VEC4: a vector starting past the clamp reads the clamp's vector instead
+  // (rows are whole vectors); all its tokens lie past L and are never used.
+  int32_t v[kNgPre][kNgPer], hv[kNgPre];
+  auto load_round = [&](int pr, int clamp_to) {
+    if constexpr (VEC4) {
+      const int4* h4 = reinterpret_cast<const int4*>(h);
 #pragma unroll
-  for (int r = 0; r < kNgPer; ++r) v[0][r] = h[min(r * kNgBlock + t, Lmax - 1)];
+      for (int q = 0; q < kNgPer / 4; ++q) {
+        const int4 x = h4[min(pr * kNgRound + ng_off<true>(4 * q, t), clamp_to & ~3) / 4];
+        v[pr][4 * q] = x.x;
+        v[pr][4 * q + 1] = x.y;
+        v[pr][4 * q + 2] = x.z;
+        v[pr][4 * q + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < kNgPer; ++r) v[pr][r] = h[min(pr * kNgRound + ng_off<false>(r, t), clamp_to)];
+    }
+  };
+  load_round(0, Lmax - 1);
   hv[0] = 0;  // before the history
   const int L = min(max(L_raw, 0), Lmax);
   const int last_tok = max(L - 1, 0);
@@ -65,8 +93,7 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
   }
 #pragma unroll
   for (int pr = 1; pr < kNgPre; ++pr) {
-#pragma unroll
-    for (int r = 0; r < kNgPer; ++r) v[pr][r] = h[min(pr * kNgRound + r * kNgBlock + t, last_tok)];
+    load_round(pr, last_tok);
     hv[pr] = h[min(max(pr * kNgRound - NM + t, 0), last_tok)];  // used by threads < NM
   }
   __shared__ int cnt[SPECV_MAX_NGRAM + 1], last[SPECV_MAX_NGRAM + 1];
@@ -83,15 +110,15 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
     l[n] = -1;
   }
   // One round: ends base .. base + kNgRound - 1, from the thread's tokens vr
-  // (vr[r] = h[base - 1 + r * kNgBlock + t]) and hvr (the NM tokens before
-  // the round, threads < NM), staged in LDS so that matches are measured
-  // without dependent global loads.
-  __shared__ int32_t win[kNgRound + SPECV_MAX_NGRAM];
+  // (vr[r] = h[base - 1 + ng_off(r, t)]) and hvr (the NM tokens before the
+  // round, threads < NM), staged in LDS so that matches are measured without
+  // dependent global loads.
+  __shared__ __align__(16) int32_t win[kNgRound + SPECV_MAX_NGRAM];
   auto round = [&](int base, const int32_t (&vr)[kNgPer], int32_t hvr) {
     const int w0 = base - 1 - NM;  // win[k] = h[w0 + k]
     __syncthreads();  // the previous round is done with win
 #pragma unroll
-    for (int r = 0; r < kNgPer; ++r) win[NM + r * kNgBlock + t] = vr[r];
+    for (int r = 0; r < kNgPer; ++r) win[NM + ng_off<VEC4>(r, t)] = vr[r];
     if (t < NM) win[t] = hvr;
     __syncthreads();
     // first tokens: bit r of `first` says whether end r's last token equals
@@ -100,18 +127,18 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
     uint32_t first = 0;
 #pragma unroll
     for (int r = 0; r < kNgPer; ++r) {
-      const int e = base + r * kNgBlock + t;
+      const int e = base + ng_off<VEC4>(r, t);
       first |= ((e < L && jmax > 0 && vr[r] == sf[0]) ? 1u : 0u) << r;
     }
     // size 1 straight from the bits (ends increase with r)
     c[0] += __popc(first);
-    if (first) l[0] = base + (31 - __clz(first)) * kNgBlock + t;
+    if (first) l[0] = base + ng_off<VEC4>(31 - __clz(first), t);
     // longer sizes: only the ends whose last token matched, in increasing order
     uint32_t more = NM > 1 ? first : 0u;
     while (more) {
       const int r = __builtin_ctz(more);
       more &= more - 1u;
-      const int e = base + r * kNgBlock + t;
+      const int e = base + ng_off<VEC4>(r, t);
       const int k = e - 1 - w0;
       // match length m(e): trailing ones of the NM comparisons (j = 0 matched),
       // cut to the sizes that exist (j < jmax and h[e-1-j] inside the history)
@@ -136,7 +163,7 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
   for (int base = 1 + kNgPre * kNgRound; base < L; base += kNgRound) {
     int32_t vt[kNgPer];
 #pragma unroll
-    for (int r = 0; r < kNgPer; ++r) vt[r] = h[min(base - 1 + r * kNgBlock + t, L - 1)];
+    for (int r = 0; r < kNgPer; ++r) vt[r] = h[min(base - 1 + ng_off<VEC4>(r, t), L - 1)];
     round(base, vt, h[min(max(base - 1 - NM + t, 0), L - 1)]);
   }
   // per size: the wave's count and latest end (DPP reductions, lane 63 holds
@@ -174,19 +201,29 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
 
 }  // namespace
 
-hipError_t launch_ngram(const int32_t* hist, const int32_t* lengths, int B, int Lmax, int n_min, int n_max,
-                        int min_hits, int K, int32_t* out_draft, int32_t* out_count, hipStream_t st) {
+template <bool VEC4>
+void launch_ngram_t(const int32_t* hist, const int32_t* lengths, int B, int Lmax, int n_min, int n_max,
+                    int min_hits, int K, int32_t* out_draft, int32_t* out_count, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(B)), block(kNgBlock);
   // counters for the sizes in use only (registers, fully unrolled)
   if (n_max <= 4)
-    hipLaunchKernelGGL(k_ngram<4>, grid, block, 0, st, hist, lengths, Lmax, n_min, n_max, min_hits, K, out_draft,
-                       out_count);
+    hipLaunchKernelGGL((k_ngram<4, VEC4>), grid, block, 0, st, hist, lengths, Lmax, n_min, n_max, min_hits, K,
+                       out_draft, out_count);
   else if (n_max <= 8)
-    hipLaunchKernelGGL(k_ngram<8>, grid, block, 0, st, hist, lengths, Lmax, n_min, n_max, min_hits, K, out_draft,
-                       out_count);
+    hipLaunchKernelGGL((k_ngram<8, VEC4>), grid, block, 0, st, hist, lengths, Lmax, n_min, n_max, min_hits, K,
+                       out_draft, out_count);
   else
-    hipLaunchKernelGGL(k_ngram<SPECV_MAX_NGRAM>, grid, block, 0, st, hist, lengths, Lmax, n_min, n_max, min_hits,
-                       K, out_draft, out_count);
+    hipLaunchKernelGGL((k_ngram<SPECV_MAX_NGRAM, VEC4>), grid, block, 0, st, hist, lengths, Lmax, n_min, n_max,
+                       min_hits, K, out_draft, out_count);
+}
+
+hipError_t launch_ngram(const int32_t* hist, const int32_t* lengths, int B, int Lmax, int n_min, int n_max,
+                        int min_hits, int K, int32_t* out_draft, int32_t* out_count, hipStream_t st) {
+  // whole 16-byte vectors per row: an aligned history and L_max a multiple of 4
+  if (reinterpret_cast<uintptr_t>(hist) % 16 == 0 && Lmax % 4 == 0)
+    launch_ngram_t<true>(hist, lengths, B, Lmax, n_min, n_max, min_hits, K, out_draft, out_count, st);
+  else
+    launch_ngram_t<false>(hist, lengths, B, Lmax, n_min, n_max, min_hits, K, out_draft, out_count, st);
   return hipGetLastError();
 }
 

@@ -67,3 +67,25 @@ def test_random_proposals_match_oracle(gpu_lib, case):
     rd, rc = ngram.propose(hist, lens, n_min, n_max, hits, K)
     np.testing.assert_array_equal(c, rc)
     np.testing.assert_array_equal(d, rd)
+
+
+def test_vector_and_element_loads_agree(gpu_lib):
+    # rows of L_max % 4 == 0 in a 16-byte aligned history are read as 16-byte
+    # vectors; the same rows one int32 off that alignment are read token by
+    # token: both must give the oracle's proposals
+    import torch
+    B, L = 48, 12288
+    hist, lens = workloads.make_histories(B, L, 50, seed=99, workers=workloads.default_workers())
+    h16 = torch.from_numpy(hist).cuda()
+    buf = torch.empty(B * L + 1, dtype=torch.int32, device="cuda")
+    buf[1:] = h16.view(-1)
+    h4 = buf[1:].view(B, L)
+    assert h16.data_ptr() % 16 == 0 and h4.data_ptr() % 16 == 4
+    ln = torch.from_numpy(lens).cuda()
+    d1, c1 = gpu_lib.ngram_propose(h16, ln, 1, 8, 1, 6)
+    d2, c2 = gpu_lib.ngram_propose(h4, ln, 1, 8, 1, 6)
+    torch.cuda.synchronize()
+    rd, rc = ngram.propose(hist, lens, 1, 8, 1, 6)
+    for d, c in ((d1, c1), (d2, c2)):
+        np.testing.assert_array_equal(c.cpu().numpy(), rc)
+        np.testing.assert_array_equal(d.cpu().numpy(), rd)
