@@ -160,6 +160,13 @@ double rounds_min_bytes() {
   return v;
 }
 
+// The first level of the last round for K drafts.
+int last_round_begin(int K) {
+  int b = 0;
+  for (int r = 0; r < kMaxRounds && round_begin(r) <= K; ++r) b = round_begin(r);
+  return b;
+}
+
 // The sweep's launches for one call: every row at once when `full`, else
 // rounds of levels (see round_begin) with k_round_accept between them; the
 // events go to the first and the last sweep launch.
@@ -310,6 +317,7 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
 
   if (launch_sweeps(P, dtype, false, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
     return SPECV_E_HIP;
+  P.vpre = full ? 0 : last_round_begin(K);
   if (launch_verify(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   if (launch_exact(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   if (position_stats && launch_position_stats(P, st) != hipSuccess) return SPECV_E_HIP;

@@ -151,6 +151,56 @@ __device__ inline SeqRec accept_scan(const Params& p, long s, bool writer) {
   return sRec;
 }
 
+// Whole wave: log2 sum_v 2^(x_v c) of row i of sequence s, folded from the
+// sweep's partials in accept_scan's order (lane l takes partials l, l + 64,
+// ...), so the value is bit for bit the one accept_scan computes for it.
+__device__ inline double fold_row(const Params& p, long s, int nrows, int i, int np) {
+  const int lane = threadIdx.x % kWave;
+  const float2* base = p.part + (s * nrows + i) * np;
+  float ml = -INFINITY;
+  double sl = 0.0;
+  for (int j = lane; j < np; j += kWave) fold_partial(ml, sl, base[j]);
+  return wave_log2z(ml, sl);
+}
+
+// After the sweep's rounds, for a sequence decided before the last round:
+// n = kbs[s] (its first rejection, or K_b with every draft accepted).
+// k_round_accept ran the acceptance tests of those positions on the same
+// partials with the same fold and test, so accept_scan would find the same n;
+// the record needs only the normalisers of the decisive rows (folded as
+// accept_scan folds them) and the tokens before n.  Wave 0 does it all, one
+// memory round trip instead of accept_scan's gathers and folds of every row.
+// Writes and returns what accept_scan would (there is no log Z to write:
+// calls that ask for it take the one-sweep path).
+template <int DT>
+__device__ inline SeqRec decided_scan(const Params& p, long s, int n, bool writer) {
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int K = p.K, nrows = 2 * K + 1, np = p.nch1 * kWaves;
+  const int kb = seq_kb(p, s);
+  __shared__ SeqRec sRecD;
+  if (w == 0) {
+    const int xk = (lane <= n && lane < kb) ? p.x[s * K + lane] : 0;
+    const double lzp = fold_row(p, s, nrows, n, np);
+    const double lzq = n < kb ? fold_row(p, s, nrows, K + 1 + n, np) : 0.0;  // uniform
+    const bool valid = xk >= 0 && xk < p.V;
+    const bool bad = n < kb && __builtin_amdgcn_readlane(valid ? 1 : 0, n < kb ? n : 0) == 0;
+    if (writer && lane <= K && lane != n) p.out_tokens[s * (K + 1) + lane] = lane < n ? xk : -1;
+    if (lane == 0) {
+      if (writer) p.out_n[s] = n;
+      SeqRec r;
+      r.n = n;
+      r.kb = kb;
+      r.flags = bad ? SPECV_FLAG_BAD_DRAFT : 0;
+      r.seq = static_cast<int32_t>(s);
+      r.lzp = lzp;
+      r.lzq = lzq;
+      sRecD = r;
+    }
+  }
+  __syncthreads();
+  return sRecD;
+}
+
 // ------------------------------------------------------------------ draw --
 // fp32 weights scaled by the common factor 2^Fp: P' = 2^(x c - Wp) and
 // Q' = 2^((y c - Wq) - D), with Wp, Wq = rint(L') whole, Fp, Fq the remaining
@@ -596,7 +646,10 @@ __global__ __launch_bounds__(kVBlock) void k_verify(Params p) {
     part = static_cast<int>(blockIdx.x - local * split);
     s = p.seq0 + local;
   }
-  const SeqRec rec = accept_scan<DT>(p, s, part == 0);
+  // uniform over the workgroup: a sequence decided before the last round
+  // needs no acceptance scan
+  const int kd = p.vpre > 0 ? p.kbs[s] : p.vpre;
+  const SeqRec rec = kd < p.vpre ? decided_scan<DT>(p, s, kd, part == 0) : accept_scan<DT>(p, s, part == 0);
   if (rec.n == rec.kb) fast_draw<DT, VEC, true, SPLIT>(p, s, rec, part);
   else fast_draw<DT, VEC, false, SPLIT>(p, s, rec, part);
 }

@@ -145,6 +145,8 @@ struct Params {
   int lv0, lv1;              // grid3: the levels the launch covers (target rows lv0..lv1-1, and the
                              // draft rows among them); lv0 > 0: skip the rows past kbs[s]
   int32_t* kbs;              // [B] rounds: the last level still to sweep per sequence (k_round_accept)
+  int vpre;                  // k_verify, rounds: the last round's first level (sequences with kbs below it
+                             // were decided earlier); 0 after a one-sweep call
   int R3, ch3;               // fp64 draw chunks per row, elements per chunk
   int seq0, nseq;            // the sequences a launch covers
   int split;                 // workgroups per sequence in k_verify (1: no split)
