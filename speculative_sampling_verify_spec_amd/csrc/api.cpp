@@ -318,6 +318,9 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   if (launch_sweeps(P, dtype, false, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
     return SPECV_E_HIP;
   P.vpre = full ? 0 : last_round_begin(K);
+  // more sequences than CUs: two smaller workgroups per CU (see launch_verify)
+  const int cus = device_cus();
+  P.vwaves = (P.split <= 1 && cus > 0 && B > cus) ? kVerifyWavesSmall : kVerifyWaves;
   if (launch_verify(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   if (launch_exact(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   if (position_stats && launch_position_stats(P, st) != hipSuccess) return SPECV_E_HIP;

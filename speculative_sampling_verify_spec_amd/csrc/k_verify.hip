@@ -2,7 +2,8 @@
 // threads per sequence runs the acceptance scan and then the fast
 // replacement / bonus draw, so no partial result has to cross workgroups.
 // When the batch is small enough to leave CUs idle, a sequence gets `split`
-// workgroups instead (see Split below).
+// workgroups instead (see Split below); when it has more sequences than CUs,
+// workgroups of 512 threads (see launch_verify_t).
 //
 // Acceptance.  The 16 waves fold the sweep's per-wave (R, s) partials of the
 // sequence's 2K+1 rows into log2 normalisers (fp64 sums with exact
@@ -55,8 +56,8 @@ namespace {
 
 constexpr int kVBlock = kVerifyBlock;         // threads per workgroup
 constexpr int kVWaves = kVerifyWaves;         // 16
+constexpr int kVWavesSmall = kVerifyWavesSmall;  // 8
 constexpr int kRowsMax = 2 * SPECV_MAX_K + 1;
-constexpr int kRowsPerWave = (kRowsMax + kVWaves - 1) / kVWaves;  // 5 rows per wave at most
 constexpr int kSplitReads = 16;  // reads of the published values before the fp64 fallback
 
 // ------------------------------------------------------------ acceptance --
@@ -64,8 +65,9 @@ constexpr int kSplitReads = 16;  // reads of the published values before the fp6
 // the padding of out_tokens (slot n is the draw's), out_n and out_logz (the
 // other workgroups of a split sequence compute the same record and write
 // nothing).  Returns the record.
-template <int DT>
+template <int DT, int NW>
 __device__ inline SeqRec accept_scan(const Params& p, long s, bool writer) {
+  constexpr int kRowsPerWave = (kRowsMax + NW - 1) / NW;  // rows each wave folds, at most
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int K = p.K, nrows = 2 * K + 1, np = p.nch1 * kWaves;  // kWaves: the sweep's waves per chunk
   const int kb = seq_kb(p, s);  // the sequence's own draft count
@@ -93,7 +95,7 @@ __device__ inline SeqRec accept_scan(const Params& p, long s, bool writer) {
     float2 q[kRowsPerWave];
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
-      const int i = w + r * kVWaves;
+      const int i = w + r * NW;
       q[r] = (i < nrows && used(i) && lane < np) ? p.part[(s * nrows + i) * np + lane] : make_float2(-INFINITY, 0.f);
     }
 #pragma unroll
@@ -106,12 +108,12 @@ __device__ inline SeqRec accept_scan(const Params& p, long s, bool writer) {
   for (int j = lane + kWave; j < np; j += kWave)  // long rows: the rest of the partials
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
-      const int i = w + r * kVWaves;
+      const int i = w + r * NW;
       if (i < nrows && used(i)) fold_partial(ml[r], sl[r], p.part[(s * nrows + i) * np + j]);
     }
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
-    const int i = w + r * kVWaves;
+    const int i = w + r * NW;
     if (i >= nrows) break;  // uniform over the wave
     if (!used(i)) continue;
     const double lz2 = wave_log2z(ml[r], sl[r]);
@@ -312,15 +314,15 @@ struct Iter {
 // Stream the decisive row(s): segment masses into segA, fp64 lane totals of
 // P' and Q'.  Per unit the sums are pairwise in fp32, then pairwise over the
 // lane's U units; the residual mass of a lane is sum P' - sum min(P', Q').
-// Segments come in blocks of kVWaves (one per wave); workgroup `part` of a
+// Segments come in blocks of NW (one per wave); workgroup `part` of a
 // sequence split over `split` takes blocks part, part + split, ...  A
 // segment's mass does not depend on which workgroup computes it.
-template <int DT, bool VEC, bool BONUS>
+template <int DT, bool VEC, bool BONUS, int NW>
 __device__ inline void stream_row(const void* rp, const void* rq, const FastWeight& wt, const Geometry<DT, VEC>& g,
                                   int part, int split, float* segA, double& tsp, double& tsq) {
   using G = Geometry<DT, VEC>;
   const int lane = threadIdx.x % kWave, w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  for (int j = part * kVWaves + w; j < g.nseg; j += kVWaves * split) {
+  for (int j = part * NW + w; j < g.nseg; j += NW * split) {
     float a = 0.f;
     for (int it = 0; it < g.iters; ++it) {
       const long base = (static_cast<long>(j) * g.iters + it) * G::kIterUnits;
@@ -491,7 +493,7 @@ __device__ inline void block_sum2_n(double& a, double& b, double* lds /* >= 2 NW
 
 // SPLIT: the sequence's stream is shared by p.split workgroups (`part` is
 // this one's index), which exchange their results through the workspace.
-template <int DT, bool VEC, bool BONUS, bool SPLIT>
+template <int DT, bool VEC, bool BONUS, bool SPLIT, int NW>
 __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec, int part) {
   using G = Geometry<DT, VEC>;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -503,18 +505,18 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec, int
   const void* rp = row_ptr<DT>(p.lp, s * (p.K + 1) + n, p.V);
   const void* rq = BONUS ? nullptr : row_ptr<DT>(p.lq, s * p.K + n, p.V);
   __shared__ float segA[kMaxSegs];
-  __shared__ double lds[2 * kVWaves];
+  __shared__ double lds[2 * NW];
 
   const int split = SPLIT ? p.split : 1;
   double tsp = 0.0, tsq = 0.0;
-  stream_row<DT, VEC, BONUS>(rp, rq, wt, g, part, split, segA, tsp, tsq);
+  stream_row<DT, VEC, BONUS, NW>(rp, rq, wt, g, part, split, segA, tsp, tsq);
   // the reductions' barriers also publish segA
   double SP = tsp, SQ = 0.0;
   if constexpr (BONUS) {
-    SP = block_sum_n<kVWaves>(tsp, lds);
+    SP = block_sum_n<NW>(tsp, lds);
   } else {
     SQ = tsq;
-    block_sum2_n<kVWaves>(SP, SQ, lds);
+    block_sum2_n<NW>(SP, SQ, lds);
   }
   if (w != 0) return;
 
@@ -530,7 +532,7 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec, int
     float* gseg = p.segm + s * g.nseg;
     double* gsum = p.spq + (s * kMaxSplit) * 2;
     for (int k = lane;; k += kWave) {  // this workgroup's k-th segment, in increasing order
-      const int j = ((k / kVWaves) * split + part) * kVWaves + k % kVWaves;
+      const int j = ((k / NW) * split + part) * NW + k % NW;
       if (j >= g.nseg) break;
       __hip_atomic_store(gseg + j, segA[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -636,8 +638,10 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec, int
 }
 
 // Workgroup g takes sequence seq0 + g (SPLIT: seq0 + g / split, part g % split).
-template <int DT, bool VEC, bool SPLIT>
-__global__ __launch_bounds__(kVBlock) void k_verify(Params p) {
+// NW waves per workgroup: kVWaves (16), or kVWavesSmall (8) when the batch
+// has more sequences than the device has CUs (see launch_verify_t).
+template <int DT, bool VEC, bool SPLIT, int NW>
+__global__ __launch_bounds__(NW * kWave) void k_verify(Params p) {
   long s = p.seq0 + blockIdx.x;
   int part = 0;
   if constexpr (SPLIT) {
@@ -649,19 +653,29 @@ __global__ __launch_bounds__(kVBlock) void k_verify(Params p) {
   // uniform over the workgroup: a sequence decided before the last round
   // needs no acceptance scan
   const int kd = p.vpre > 0 ? p.kbs[s] : p.vpre;
-  const SeqRec rec = kd < p.vpre ? decided_scan<DT>(p, s, kd, part == 0) : accept_scan<DT>(p, s, part == 0);
-  if (rec.n == rec.kb) fast_draw<DT, VEC, true, SPLIT>(p, s, rec, part);
-  else fast_draw<DT, VEC, false, SPLIT>(p, s, rec, part);
+  const SeqRec rec =
+      kd < p.vpre ? decided_scan<DT>(p, s, kd, part == 0) : accept_scan<DT, NW>(p, s, part == 0);
+  if (rec.n == rec.kb) fast_draw<DT, VEC, true, SPLIT, NW>(p, s, rec, part);
+  else fast_draw<DT, VEC, false, SPLIT, NW>(p, s, rec, part);
 }
 
+// One 1024-thread workgroup of k_verify fills a CU (its registers), so a
+// batch of more sequences than CUs would run in generations that each wait
+// for their slowest sequence, every workgroup's acceptance and select phases
+// exposed.  There (p.vwaves == kVWavesSmall) 512-thread workgroups let two
+// sequences share a CU, one's latency phases overlapping the other's stream.
+// Segment masses do not depend on which wave computes them, so both shapes
+// draw the same tokens.
 template <int DT, bool VEC>
 void launch_verify_t(const Params& p, hipStream_t st) {
-  const dim3 block(kVBlock);
   const unsigned n = static_cast<unsigned>(p.nseq);
   if (p.split > 1)
-    hipLaunchKernelGGL((k_verify<DT, VEC, true>), dim3(n * static_cast<unsigned>(p.split)), block, 0, st, p);
+    hipLaunchKernelGGL((k_verify<DT, VEC, true, kVWaves>), dim3(n * static_cast<unsigned>(p.split)), dim3(kVBlock), 0,
+                       st, p);
+  else if (p.vwaves == kVWavesSmall)
+    hipLaunchKernelGGL((k_verify<DT, VEC, false, kVWavesSmall>), dim3(n), dim3(kVWavesSmall * kWave), 0, st, p);
   else
-    hipLaunchKernelGGL((k_verify<DT, VEC, false>), dim3(n), block, 0, st, p);
+    hipLaunchKernelGGL((k_verify<DT, VEC, false, kVWaves>), dim3(n), dim3(kVBlock), 0, st, p);
 }
 
 }  // namespace

@@ -47,6 +47,7 @@ constexpr double kRoundsMinBytes = 256.0 * (1 << 20);
 // split workspace and picks the split from it.
 constexpr int kVerifyBlock = 1024;            // threads per k_verify workgroup
 constexpr int kVerifyWaves = kVerifyBlock / kWave;
+constexpr int kVerifyWavesSmall = 8;  // k_verify's waves per workgroup for batches of more sequences than CUs
 constexpr int kMaxSegs = 1024;                // segments per row, at most
 __host__ __device__ constexpr int draw_lane_units(bool vec) { return vec ? 2 : 8; }
 
@@ -145,6 +146,7 @@ struct Params {
   int lv0, lv1;              // grid3: the levels the launch covers (target rows lv0..lv1-1, and the
                              // draft rows among them); lv0 > 0: skip the rows past kbs[s]
   int32_t* kbs;              // [B] rounds: the last level still to sweep per sequence (k_round_accept)
+  int vwaves;                // k_verify's waves per workgroup when unsplit: kVerifyWaves or kVerifyWavesSmall
   int vpre;                  // k_verify, rounds: the last round's first level (sequences with kbs below it
                              // were decided earlier); 0 after a one-sweep call
   int R3, ch3;               // fp64 draw chunks per row, elements per chunk

@@ -394,3 +394,22 @@ def test_resample_uniform_at_the_ends_of_its_grid(gpu_lib):
     compare(b2, g, ref).check()
     same = np.flatnonzero(g.n == ref.n_accepted)
     np.testing.assert_array_equal(g.tokens[same], ref.tokens[same])
+
+
+@pytest.mark.parametrize("nseq,V,ragged", [(320, None, False), (300, 31999, False), (288, None, True)],
+                         ids=["bf16-vector", "bf16-element-loads", "bf16-vector-ragged"])
+def test_more_sequences_than_cus(gpu_lib, nseq, V, ragged):
+    """Batches of more sequences than the MI355X's 256 CUs take k_verify's
+    512-thread shape (two sequences per CU): the small workload's recipe at
+    B = 288-320, with 16-byte vector loads and, at V = 31999, element loads,
+    and once with per-sequence draft counts; every sequence against the
+    oracle."""
+    b = workloads.make_batch(1, seqs=range(nseq), workers=workloads.default_workers(), V=V)
+    if ragged:
+        b = dataclasses.replace(b, num_drafts=workloads.ragged_draft_counts(b.B, b.K, seed=5, low=0))
+    say(f"[parity] {nseq} sequences, V={b.V}, ragged={ragged}")
+    g = run_gpu(gpu_lib, b)
+    rep = compare(b, g, oracle.verify_batch(b, workers=workloads.default_workers()))
+    say(f"[parity] {nseq} sequences: decisions={rep.decisions} excused={rep.excused} "
+        f"max_logz_err={rep.max_logz_err:.2e}")
+    rep.check()
