@@ -8,6 +8,7 @@ fallback: a missing library raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -108,10 +109,9 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float,
-                out_tokens=None, out_n_accepted=None, workspace=None, *,
-                out_logz=None, out_flags=None, events=None, stream=None, extended: bool = False) -> int:
-    """Raw call with caller-provided device tensors; returns the library's status code."""
+def _spec_verify_call(logits_p, logits_q, draft_tokens, u_accept, u_resample, T, out_tokens, out_n_accepted,
+                      workspace, out_logz, out_flags, events, stream, extended):
+    """The library function and its argument list for one spec_verify(_ex) call."""
     lib = load()
     B, K1, V = logits_p.shape
     K = K1 - 1
@@ -122,9 +122,35 @@ def spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float
             float(T), B, K, V, _ptr(out_tokens), _ptr(out_n_accepted), dt,
             _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(), st]
     if not extended and out_logz is None and out_flags is None and events is None:
-        return int(lib.spec_verify(*args))
+        return lib.spec_verify, args
     e0, e1 = events if events is not None else (None, None)
-    return int(lib.spec_verify_ex(*args, _ptr(out_logz), _ptr(out_flags), e0, e1))
+    return lib.spec_verify_ex, args + [_ptr(out_logz), _ptr(out_flags), e0, e1]
+
+
+def spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float,
+                out_tokens=None, out_n_accepted=None, workspace=None, *,
+                out_logz=None, out_flags=None, events=None, stream=None, extended: bool = False) -> int:
+    """Raw call with caller-provided device tensors; returns the library's status code."""
+    fn, args = _spec_verify_call(logits_p, logits_q, draft_tokens, u_accept, u_resample, T, out_tokens,
+                                 out_n_accepted, workspace, out_logz, out_flags, events, stream, extended)
+    return int(fn(*args))
+
+
+def _bound(fn, args):
+    """fn with its arguments converted to ctypes values once."""
+    conv = [t(a) if a is not None else None for t, a in zip(fn.argtypes, args)]
+    return functools.partial(fn, *conv)
+
+
+def bind_spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float,
+                     out_tokens=None, out_n_accepted=None, workspace=None, *,
+                     out_logz=None, out_flags=None, stream=None, extended: bool = False):
+    """spec_verify's arguments marshalled once: returns a function of no
+    arguments that enqueues the same call again and returns its status code,
+    for loops over resident buffers (the tensors must stay alive and in
+    place)."""
+    return _bound(*_spec_verify_call(logits_p, logits_q, draft_tokens, u_accept, u_resample, T, out_tokens,
+                                     out_n_accepted, workspace, out_logz, out_flags, None, stream, extended))
 
 
 def spec_verify_noalloc(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, out_tokens,
@@ -145,6 +171,24 @@ def spec_verify_ragged(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u
                        out_logz=None, out_flags=None, stream=None) -> int:
     """Raw call of spec_verify_ragged (spec_verify_ragged_ex when log Z or
     flags are asked for); returns the library's status code."""
+    fn, args = _spec_verify_ragged_call(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T,
+                                        out_tokens, out_n_accepted, workspace, position_stats, out_logz, out_flags,
+                                        stream)
+    return int(fn(*args))
+
+
+def bind_spec_verify_ragged(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T: float,
+                            out_tokens=None, out_n_accepted=None, workspace=None, *, position_stats=None,
+                            out_logz=None, out_flags=None, stream=None):
+    """spec_verify_ragged's arguments marshalled once (see bind_spec_verify)."""
+    return _bound(*_spec_verify_ragged_call(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T,
+                                            out_tokens, out_n_accepted, workspace, position_stats, out_logz,
+                                            out_flags, stream))
+
+
+def _spec_verify_ragged_call(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u_resample, T, out_tokens,
+                             out_n_accepted, workspace, position_stats, out_logz, out_flags, stream):
+    """The library function and its argument list for one spec_verify_ragged(_ex) call."""
     lib = load()
     B, K1, V = logits_p.shape
     import torch
@@ -154,8 +198,8 @@ def spec_verify_ragged(logits_p, logits_q, draft_tokens, num_drafts, u_accept, u
             _ptr(position_stats), _dtype_code(logits_p), _ptr(workspace),
             0 if workspace is None else workspace.numel() * workspace.element_size(), st]
     if out_logz is None and out_flags is None:
-        return int(lib.spec_verify_ragged(*args))
-    return int(lib.spec_verify_ragged_ex(*args, _ptr(out_logz), _ptr(out_flags)))
+        return lib.spec_verify_ragged, args
+    return lib.spec_verify_ragged_ex, args + [_ptr(out_logz), _ptr(out_flags)]
 
 
 def verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, *,

@@ -413,3 +413,37 @@ def test_more_sequences_than_cus(gpu_lib, nseq, V, ragged):
     say(f"[parity] {nseq} sequences: decisions={rep.decisions} excused={rep.excused} "
         f"max_logz_err={rep.max_logz_err:.2e}")
     rep.check()
+
+
+def test_bound_calls_match(gpu_lib):
+    """bind_spec_verify / bind_spec_verify_ragged (arguments marshalled once,
+    as bench.py times them) enqueue the same calls: the same outputs as
+    spec_verify / spec_verify_ragged, on every repeat."""
+    import torch
+    sv = gpu_lib
+    b = workloads.make_batch(1, seqs=range(48), workers=workloads.default_workers())
+    lp, lq, x, ua, ur = to_device(b)
+    B, K, V, T = b.B, b.K, b.V, b.T
+    ws = torch.empty(sv.workspace_size(B, K, V, sv.SPECV_BF16, T), dtype=torch.uint8, device="cuda")
+    kb = torch.from_numpy(workloads.ragged_draft_counts(B, K, seed=9, low=0)).cuda()
+    outs = {}
+    for name in ("plain", "bound", "ragged", "ragged-bound"):
+        tok = torch.full((B, K + 1), -7, dtype=torch.int32, device="cuda")
+        n = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        fl = torch.zeros((B,), dtype=torch.int32, device="cuda")
+        if name == "plain":
+            rcs = [sv.spec_verify(lp, lq, x, ua, ur, T, tok, n, ws, out_flags=fl, extended=True)]
+        elif name == "bound":
+            call = sv.bind_spec_verify(lp, lq, x, ua, ur, T, tok, n, ws, out_flags=fl, extended=True)
+            rcs = [call() for _ in range(3)]
+        elif name == "ragged":
+            rcs = [sv.spec_verify_ragged(lp, lq, x, kb, ua, ur, T, tok, n, ws, out_flags=fl)]
+        else:
+            call = sv.bind_spec_verify_ragged(lp, lq, x, kb, ua, ur, T, tok, n, ws, out_flags=fl)
+            rcs = [call() for _ in range(3)]
+        torch.cuda.synchronize()
+        assert rcs == [0] * len(rcs), rcs
+        outs[name] = (tok.cpu().numpy(), n.cpu().numpy(), fl.cpu().numpy() & ~sv.FLAG_FP64)
+    for a, c in (("plain", "bound"), ("ragged", "ragged-bound")):
+        for u, v in zip(outs[a], outs[c]):
+            np.testing.assert_array_equal(u, v, err_msg=f"{a} vs {c}")
