@@ -321,6 +321,23 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   // more sequences than CUs: two smaller workgroups per CU (see launch_verify)
   const int cus = device_cus();
   P.vwaves = (P.split <= 1 && cus > 0 && B > cus) ? kVerifyWavesSmall : kVerifyWaves;
+  // at most half the CUs busy with sequences: the rest compute every
+  // sequence's fp64 chunk sums during the fast draw, at most kEagerMaxRounds
+  // chunks per 128-thread group (see k_verify)
+  P.xeager = 0;
+  P.xper = 0;
+  if (P.split <= 1 && P.vwaves == kVerifyWaves && cus > 0 && P.R3 > kSoloMaxChunks) {
+    const int spare = cus / B - 1;  // workgroups per sequence besides its own
+    const int groups = kVerifyBlock / kXBlock;
+    if (spare >= 1) {
+      const int xe = std::min(spare, (P.R3 + groups - 1) / groups);
+      const int per = (P.R3 + xe - 1) / xe;
+      if ((per + groups - 1) / groups <= kEagerMaxRounds) {
+        P.xeager = xe;
+        P.xper = per;
+      }
+    }
+  }
   if (launch_verify(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   if (launch_exact(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
   if (position_stats && launch_position_stats(P, st) != hipSuccess) return SPECV_E_HIP;

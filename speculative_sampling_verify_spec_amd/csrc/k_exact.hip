@@ -8,7 +8,9 @@
 //
 // Two kernels walk the queue the fast draw filled (each entry is the
 // sequence's whole record, read together with the queue's length); rows of
-// at most two chunks take one kernel that does both (k_exact_solo):
+// at most two chunks take one kernel that does both (k_exact_solo), and on
+// small batches k_verify's spare workgroups have already computed every
+// sequence's chunk sums, so the select runs alone (k_exact_select_seq):
 //   exact_chunks (queued sequences x chunks of ch3 >= 1024 tokens): per chunk
 //        sum P, sum Q, A = sum max(0, P - Q), G = sum_{P > Q} Q and
 //        H = sum_{near flip} Q, the Q-mass within a relative kKappa of P = Q.
@@ -26,136 +28,16 @@
 // draw takes the last token with positive weight; a residual of zero mass
 // (p == q to rounding) falls back to p_n and sets a flag.
 #include "sv_device.h"
+#include "sv_exact.h"
 #include "specverify.h"
 
 namespace sv {
 
 namespace {
 
-constexpr int kXBlock = 128;                     // threads of every workgroup here
-constexpr int kXWaves = kXBlock / kWave;
-constexpr int kRun = 8;                          // elements per lane per rescan round (a whole bf16 vector)
-constexpr int kRound = kXBlock * kRun;           // 1024 elements per round (the smallest chunk)
-constexpr double kKappa = 1e-4;                  // near-flip window, relative to Q
 constexpr unsigned kExactSeqs = 32;              // queued sequences the kernels cover per pass
-constexpr int kSoloMaxChunks = 2;                // rows of at most this many chunks: one launch (k_exact_solo)
 constexpr unsigned kSoloSeqs = 256;              // queued sequences k_exact_solo covers per pass
 constexpr int kMaxPer = (kMaxDrawChunks + kWave - 1) / kWave;  // chunks per lane in the select
-
-// fp64 weight exp(x / T - L'), L' the natural-log reference.
-struct ExactWeight {
-  double inv_t, ap, aq;
-  ExpConsts ec;
-  __device__ double P(float x) const { return exp_f64(static_cast<double>(x) * inv_t - ap, ec); }
-  __device__ double Q(float x) const { return exp_f64(static_cast<double>(x) * inv_t - aq, ec); }
-};
-
-__device__ inline ExactWeight exact_weight(const Params& p, const SeqRec& rec) {
-  ExactWeight e;
-  e.inv_t = p.inv_t;
-  e.ec = p.ec;
-  e.ap = rec.lzp * M_LN2;
-  e.aq = rec.lzq * M_LN2;
-  return e;
-}
-
-template <int DT>
-struct Rows {
-  const void* rp;
-  const void* rq;  // null for a bonus draw
-};
-
-template <int DT>
-__device__ inline Rows<DT> decisive_rows(const Params& p, long s, const SeqRec& rec) {
-  Rows<DT> r;
-  r.rp = row_ptr<DT>(p.lp, s * (p.K + 1) + rec.n, p.V);
-  r.rq = rec.n == rec.kb ? nullptr : row_ptr<DT>(p.lq, s * p.K + rec.n, p.V);
-  return r;
-}
-
-// ------------------------------------------------------------ chunk sums --
-// Chunk r of the decisive row(s) -> out[0..4] = sum P, sum Q, A, G, H (only
-// out[0] for a bonus draw).  Loads go out branch-free, U units per lane, and
-// are widened one unit at a time; the five sums are reduced over the
-// workgroup together.
-template <int DT, bool VEC>
-__device__ inline void exact_chunk_sums(const Params& p, const Rows<DT>& rows, const ExactWeight& wt, bool bonus,
-                                        int r, double* out) {
-  const long lo = static_cast<long>(r) * p.ch3;
-  const long hi = min(static_cast<long>(p.V), lo + p.ch3);
-  constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  constexpr int U = 8 / PV;  // eight elements per lane per iteration
-  const long ulo = lo / PV, uhi = hi / PV;  // VEC: lo and hi are multiples of PV
-  double acc[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
-  for (long r0 = ulo; r0 < uhi; r0 += static_cast<long>(kXBlock) * U) {
-    uint4 rp[VEC ? U : 1], rq[VEC ? U : 1];
-    float sp_[VEC ? 1 : U], sq_[VEC ? 1 : U];
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const long u = r0 + threadIdx.x + static_cast<long>(i) * kXBlock;
-      if constexpr (VEC) {
-        const long uu = u < uhi ? u : uhi - 1;
-        rp[i] = load16(rows.rp, uu);
-        if (!bonus) rq[i] = load16(rows.rq, uu);
-      } else {
-        sp_[i] = load_masked<DT>(rows.rp, u, uhi);
-        sq_[i] = bonus ? -INFINITY : load_masked<DT>(rows.rq, u, uhi);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      float ep[PV], eq[PV];
-      if constexpr (VEC) {
-        Elt<DT>::unpack(rp[i], ep);
-        if (!bonus) Elt<DT>::unpack(rq[i], eq);
-        if (bonus || r0 + threadIdx.x + static_cast<long>(i) * kXBlock >= uhi) {
-#pragma unroll
-          for (int k = 0; k < PV; ++k) eq[k] = -INFINITY;
-        }
-        if (r0 + threadIdx.x + static_cast<long>(i) * kXBlock >= uhi) {
-#pragma unroll
-          for (int k = 0; k < PV; ++k) ep[k] = -INFINITY;
-        }
-      } else {
-        ep[0] = sp_[i];
-        eq[0] = sq_[i];
-      }
-      double sp = 0.0, sq = 0.0, a = 0.0, g = 0.0, h = 0.0;
-#pragma unroll
-      for (int k = 0; k < PV; ++k) {
-        const double P = wt.P(ep[k]);
-        const double Q = wt.Q(eq[k]);  // 0 for -inf
-        const double d = P - Q;
-        sp += P;
-        sq += Q;
-        a += d > 0.0 ? d : 0.0;
-        g += d > 0.0 ? Q : 0.0;
-        h += (d <= kKappa * Q && -d <= kKappa * Q) ? Q : 0.0;
-      }
-      acc[0] += sp;
-      acc[1] += sq;
-      acc[2] += a;
-      acc[3] += g;
-      acc[4] += h;
-    }
-  }
-  __shared__ double lds[kXWaves][5];
-  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-#pragma unroll
-  for (int k = 0; k < 5; ++k) acc[k] = wave_sum(acc[k]);
-  __syncthreads();  // the previous item's reads of lds are done
-  if (lane == 0) {
-#pragma unroll
-    for (int k = 0; k < 5; ++k) lds[w][k] = acc[k];
-  }
-  __syncthreads();
-  if (threadIdx.x < 5) {
-    double t = 0.0;
-#pragma unroll
-    for (int i = 0; i < kXWaves; ++i) t += lds[i][threadIdx.x];
-    if (!bonus || threadIdx.x == 0) out[threadIdx.x] = t;
-  }
-}
 
 // A lane's run of kRun consecutive logits from v0, -inf at and past chi.
 // VEC: v0 and chi are multiples of the vector width, so whole 16-byte units
@@ -197,12 +79,19 @@ __device__ inline ChunkSums load_chunk_sums(const Params& p, long slot) {
   ChunkSums cv;
   const double* base = p.xsum + (p.seq0 + slot) * p.R3 * 5;
   const int lane = threadIdx.x % kWave, per = (p.R3 + kWave - 1) / kWave;
+  // branch-free: every lane loads (outside the row, the first chunk's sums
+  // again) and masks, so all loads are in flight together.  Relaxed atomic
+  // loads, which the compiler keeps where they are written: callers load
+  // these ahead of the test that decides whether they are needed.
 #pragma unroll
   for (int k = 0; k < kMaxPer; ++k) {
     const int c = lane * per + k;
     const bool in = threadIdx.x < kWave && k < per && c < p.R3;
 #pragma unroll
-    for (int f = 0; f < 5; ++f) cv.v[k][f] = in ? base[c * 5 + f] : 0.0;
+    for (int f = 0; f < 5; ++f) {
+      const double x = __hip_atomic_load(base + (in ? c : 0) * 5 + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      cv.v[k][f] = in ? x : 0.0;
+    }
   }
   return cv;
 }
@@ -446,6 +335,27 @@ __global__ __launch_bounds__(kXBlock) void k_exact_select(Params p) {
   }
 }
 
+// After k_verify computed every sequence's chunk sums (p.xeager > 0): one
+// workgroup per sequence of the launch, whose record (seq < 0: the fast draw
+// stood) and chunk sums are read together, by sequence.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kXBlock) void k_exact_select_seq(Params p) {
+  const long b = blockIdx.x;
+  const SeqRec rec = p.queue[p.seq0 + b];
+  const ChunkSums cv = load_chunk_sums(p, b);
+  if (rec.seq < 0) return;  // uniform
+  const long s = rec.seq;
+  const bool bonus = rec.n == rec.kb;
+  int token;
+  bool zw_zero;
+  select_exact<DT, VEC>(p, decisive_rows<DT>(p, s, rec), exact_weight(p, rec), bonus, cv,
+                        static_cast<double>(p.ur[s]), &token, &zw_zero);
+  if (threadIdx.x == 0) {
+    p.out_tokens[s * (p.K + 1) + rec.n] = token;
+    if (p.out_flags && zw_zero) p.out_flags[s] |= SPECV_FLAG_ZW_ZERO;
+  }
+}
+
 // Rows of at most kSoloMaxChunks chunks (V <= 2048): one workgroup per
 // queued sequence computes every chunk's sums itself, into LDS, and makes
 // the draw, so the fp64 draw takes one launch (its fixed cost is most of a
@@ -489,6 +399,10 @@ template <int DT, bool VEC>
 void launch_all(const Params& p, hipStream_t st) {
   const dim3 block(kXBlock);
   const unsigned ns = static_cast<unsigned>(p.nseq);
+  if (p.xeager > 0) {
+    hipLaunchKernelGGL((k_exact_select_seq<DT, VEC>), dim3(ns), block, 0, st, p);
+    return;
+  }
   if (p.R3 <= kSoloMaxChunks) {
     hipLaunchKernelGGL((k_exact_solo<DT, VEC>), dim3(ns < kSoloSeqs ? ns : kSoloSeqs), block, 0, st, p);
     return;

@@ -47,7 +47,12 @@
 //    token's interval than a certified bound (fast_bound); otherwise the
 //    sequence joins the queue of the fp64 draw, which also takes the rare
 //    cases of zero residual mass and of t at or past the end.
+//  - Chunk sums ahead.  A batch of at most half as many sequences as CUs
+//    leaves CUs idle: more workgroups of this kernel compute the fp64 draw's
+//    chunk sums of every sequence meanwhile (see eager_chunks), so that the
+//    fp64 draw of the few uncertain ones needs only its select.
 #include "sv_device.h"
+#include "sv_exact.h"
 #include "specverify.h"
 
 namespace sv {
@@ -628,12 +633,43 @@ __device__ inline void fast_draw(const Params& p, long s, const SeqRec& rec, int
   }
   if (lane == 0) {
     if (p.out_flags) p.out_flags[s] = rec.flags | (certain ? 0 : SPECV_FLAG_FP64);
-    if (certain) {
-      p.out_tokens[s * (p.K + 1) + rec.n] = token;
-    } else {
+    if (certain) p.out_tokens[s * (p.K + 1) + rec.n] = token;
+    if (p.xeager > 0) {  // every sequence's outcome, by sequence (see eager_chunks)
+      SeqRec q = rec;
+      if (certain) q.seq = -1;
+      p.queue[s] = q;
+    } else if (!certain) {
       const uint32_t slot = atomicAdd(&p.qcount[0], 1u);
       p.queue[p.seq0 + slot] = rec;
     }
+  }
+}
+
+// Small batches leave most CUs idle while the fast draws run.  There
+// (p.xeager > 0) workgroup nseq + e, e = i * xeager + part, computes the fp64
+// draw's chunk sums of sequence seq0 + i for chunks part * xper .. + xper - 1,
+// 128 threads per chunk, whether or not the fast draw will need them: the
+// acceptance scan first (the same record as the sequence's own workgroup;
+// it writes nothing), then the sums into xsum by sequence.  The fp64 draw
+// then needs only its select (k_exact.hip), and the sums are those its own
+// chunk kernel would compute.
+template <int DT, bool VEC, int NW>
+__device__ inline void eager_chunks(const Params& p, long e) {
+  constexpr int kGroups = NW * kWave / kXBlock;
+  const long local = e / p.xeager;
+  const int part = static_cast<int>(e - local * p.xeager);
+  const long s = p.seq0 + local;
+  const int kd = p.vpre > 0 ? p.kbs[s] : p.vpre;
+  const SeqRec rec = kd < p.vpre ? decided_scan<DT>(p, s, kd, false) : accept_scan<DT, NW>(p, s, false);
+  const bool bonus = rec.n == rec.kb;
+  const Rows<DT> rows = decisive_rows<DT>(p, s, rec);
+  const ExactWeight wt = exact_weight(p, rec);
+  const int grp = static_cast<int>(threadIdx.x / kXBlock);
+  const int r0 = part * p.xper, r1 = min(p.R3, r0 + p.xper);
+  double* out = p.xsum + s * p.R3 * 5;
+  for (int r = r0; r < r1; r += kGroups) {  // the same trip count for every group
+    const int rg = r + grp;
+    exact_chunk_sums<DT, VEC>(p, rows, wt, bonus, rg < r1 ? rg : p.R3, rg < r1 ? out + rg * 5 : nullptr);
   }
 }
 
@@ -644,6 +680,12 @@ template <int DT, bool VEC, bool SPLIT, int NW>
 __global__ __launch_bounds__(NW * kWave) void k_verify(Params p) {
   long s = p.seq0 + blockIdx.x;
   int part = 0;
+  if constexpr (!SPLIT && NW == kVWaves) {
+    if (static_cast<long>(blockIdx.x) >= p.nseq) {  // xeager > 0 (uniform over the workgroup)
+      eager_chunks<DT, VEC, NW>(p, blockIdx.x - p.nseq);
+      return;
+    }
+  }
   if constexpr (SPLIT) {
     const uint32_t split = static_cast<uint32_t>(p.split);
     const uint32_t local = blockIdx.x / split;
@@ -674,8 +716,9 @@ void launch_verify_t(const Params& p, hipStream_t st) {
                        st, p);
   else if (p.vwaves == kVWavesSmall)
     hipLaunchKernelGGL((k_verify<DT, VEC, false, kVWavesSmall>), dim3(n), dim3(kVWavesSmall * kWave), 0, st, p);
-  else
-    hipLaunchKernelGGL((k_verify<DT, VEC, false, kVWaves>), dim3(n), dim3(kVBlock), 0, st, p);
+  else  // and the chunk-sum workgroups when xeager > 0
+    hipLaunchKernelGGL((k_verify<DT, VEC, false, kVWaves>), dim3(n * (1u + static_cast<unsigned>(p.xeager))),
+                       dim3(kVBlock), 0, st, p);
 }
 
 }  // namespace

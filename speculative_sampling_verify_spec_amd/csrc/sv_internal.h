@@ -11,6 +11,9 @@ constexpr int kBlock = 256;   // threads per workgroup in every kernel
 constexpr int kWave = 64;     // CDNA wavefront width
 constexpr int kWaves = kBlock / kWave;
 constexpr int kMaxDrawChunks = 256;   // fp64 draw chunks per row: one wave combines them, 4 per lane
+constexpr int kXBlock = 128;          // threads that compute one fp64 draw chunk's sums
+constexpr int kSoloMaxChunks = 2;     // rows of at most this many fp64 draw chunks: one fp64 launch (k_exact_solo)
+constexpr int kEagerMaxRounds = 4;    // k_verify's chunk-sum workgroups: at most this many chunks per group of 128 threads
 
 // Elements one lane of a row sweep holds: 16-byte units on the vector path,
 // sixteen single elements on the scalar path.  The vector path has two
@@ -135,9 +138,9 @@ struct Params {
   int32_t* out_flags;        // [B] or null
   // workspace
   float2* part;              // [rows][nch1][kWaves] (R, s) sweep partials, or (max, index bits) in greedy mode
-  double* xsum;              // [B][R3][5] exact draw chunk sums (queued sequences)
+  double* xsum;              // [B][R3][5] exact draw chunk sums (by queue slot; by sequence if xeager)
   uint32_t* qcount;          // [1] sequences queued for the exact draw
-  SeqRec* queue;             // [B] their records (from the first sequence of the launch on)
+  SeqRec* queue;             // [B] their records (from the first sequence of the launch on; by sequence if xeager)
   int nch1, ch1;             // sweep chunks per row, elements per sweep chunk (at most)
   int cq, cr;                // sweep chunk c spans c*cq + min(c, cr) .. + cq + (c < cr) units
   int sweep_large;           // the sweep runs its large shape (see kSweepElems)
@@ -150,6 +153,11 @@ struct Params {
   int vpre;                  // k_verify, rounds: the last round's first level (sequences with kbs below it
                              // were decided earlier); 0 after a one-sweep call
   int R3, ch3;               // fp64 draw chunks per row, elements per chunk
+  int xeager;                // > 0: k_verify launches xeager more workgroups per sequence that compute the
+                             // fp64 draw's chunk sums of every sequence (xper chunks each) into xsum by
+                             // sequence, and the fast draw leaves every sequence's record in queue[s]
+                             // (seq < 0: drawn); 0: sums of queued sequences only, by queue slot
+  int xper;                  // xeager: chunks per workgroup
   int seq0, nseq;            // the sequences a launch covers
   int split;                 // workgroups per sequence in k_verify (1: no split)
   int nseg;                  // segments of the fast draw's row stream (seg_geom)

@@ -69,3 +69,38 @@ def test_draws_at_an_edge_go_to_fp64_and_match(gpu_lib, cfg, nseq, V):
     same = chosen[g.n[chosen] == ref2.n_accepted[chosen]]
     np.testing.assert_array_equal(g.tokens[same], ref2.tokens[same])
     compare(b2, g, ref2).check()
+
+
+def _head(b, m):
+    """The first m sequences of a batch."""
+    return dataclasses.replace(b, wl=dataclasses.replace(b.wl, B=m), seqs=b.seqs[:m], logits_p=b.logits_p[:m],
+                               logits_q=None if b.logits_q is None else b.logits_q[:m],
+                               draft_tokens=b.draft_tokens[:m], u_accept=b.u_accept[:m],
+                               u_resample=b.u_resample[:m])
+
+
+@pytest.mark.parametrize("cfg,V", [(1, None), (1, 4001), (0, 6000)],
+                         ids=["small-bf16", "V4001-bf16-scalar", "V6000-fp32"])
+def test_sums_ahead_match_the_queued_path(gpu_lib, cfg, V):
+    """Batches of at most half as many sequences as CUs compute every
+    sequence's fp64 chunk sums in k_verify's spare workgroups, and the fp64
+    draw runs its select alone; larger batches queue the uncertain draws and
+    run both fp64 kernels.  The same 64 sequences, with edge uniforms that
+    send many of them to the fp64 draw, drawn both ways (alone, and among
+    320) give the same tokens, counts and flags bit for bit, and the
+    oracle's."""
+    b = workloads.make_batch(cfg, seqs=range(320), workers=workloads.default_workers(), V=V)
+    ref = oracle.verify_batch(b, workers=workloads.default_workers())
+    ur, chosen, _ = edge_uniforms(b, ref)
+    b2 = dataclasses.replace(b, u_resample=ur)
+    print(f"cfg {cfg} V={b.V}: 320 sequences, {len(chosen)} edge uniforms", flush=True)
+    big = run_gpu(gpu_lib, b2)
+    small = _head(b2, 64)
+    g = run_gpu(gpu_lib, small)
+    c64 = chosen[chosen < 64]
+    assert len(c64) >= 16
+    assert np.all(g.flags[c64] & sv.FLAG_FP64), "an edge draw was certified by the fp32 path"
+    np.testing.assert_array_equal(g.tokens, big.tokens[:64])
+    np.testing.assert_array_equal(g.n, big.n[:64])
+    np.testing.assert_array_equal(g.flags, big.flags[:64])
+    compare(small, g, oracle.verify_batch(small)).check()
