@@ -9,14 +9,17 @@
 // the 16 before them are staged in LDS from registers filled by coalesced
 // loads: 16-byte vectors of four consecutive tokens per lane when the rows
 // allow it (L_max a multiple of 4, an aligned history), which measured far
-// faster than one token per lane, else single tokens.  The loads of the first four rounds (histories up to 16385 tokens)
-// all go out before the first round, so that rounds do not wait for memory
-// one after another; longer histories load their later rounds one at a time.
-// Each thread first compares the last token of its ends with the suffix's
-// (one compare per end, a bit mask); size 1 is counted from the mask, and
-// only the ends that passed go on to the remaining comparisons, whose run of
-// matches m(e) is counted for every size n <= m(e) in per-thread registers
-// (count and latest end per size, compiled for the largest size in use);
+// faster than one token per lane, else single tokens.  The suffix is loaded
+// first, then the first four rounds (histories up to 16385 tokens) all before
+// the first round, so that rounds do not wait for memory one after another;
+// longer histories load their later rounds one at a time.
+// Each thread compares the last token of each of its ends with the suffix's
+// last token, and the token before it with the suffix's second-last (from
+// the thread's own registers inside a 16-byte vector, else from LDS): two bit
+// masks per thread, which count sizes 1 and 2.  Only the ends that matched
+// both go on to the remaining comparisons, whose run of matches m(e) is
+// counted for every size n <= m(e) in per-thread registers (count and latest
+// end per size, compiled for the largest size in use);
 // DPP wave reductions and LDS atomics gather one value per wave.
 // Thread 0 takes the largest n in [n_min, n_max] seen at least min_hits
 // times, and the workgroup writes h[e*..min(e* + K, L)) for its latest end
@@ -50,17 +53,16 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
   const int t = static_cast<int>(threadIdx.x);
   const int lane = t % kWave;
   const int L_raw = lengths[b];
-  // Memory order: every load the rounds use is issued before the first
-  // round, so no round waits for memory once the one before it is done.
-  // All history loads are branch-free (indices clamped; tokens at or past L,
-  // and before the history, are never counted): a load under a branch makes
-  // the compiler wait for every load in flight.
-  //  - round 0's tokens right away, clamped into the row (L_max), so they
-  //    need not wait for the length;
-  //  - the suffix, the same for every lane, by scalar loads, which are
-  //    counted apart from the vector loads (waiting for it does not wait for
-  //    the tokens);
-  //  - the tokens of rounds 1 .. kNgPre - 1, clamped to the last token.
+  // Memory order.  All history loads are branch-free (indices clamped;
+  // tokens at or past L, and before the history, are never counted): a load
+  // under a branch makes the compiler wait for every load in flight.  After
+  // the length (a scalar load):
+  //  - the suffix, by one vector load ahead of all others (lane j < NM reads
+  //    h[L-1-j]); vector loads complete in order, so waiting for it waits
+  //    for nothing else;
+  //  - the tokens of rounds 0 .. kNgPre - 1, clamped to the last token, all
+  //    issued before the first round, so that no round waits for memory
+  //    once the one before it is done.
   // round pr's tokens h[pr * kNgRound + ng_off(r, t)], and the NM before it.
   // VEC4: a vector starting past the clamp reads the clamp's vector instead
   // (rows are whole vectors); all its tokens lie past L and are never used.
@@ -81,16 +83,12 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
       for (int r = 0; r < kNgPer; ++r) v[pr][r] = h[min(pr * kNgRound + ng_off<false>(r, t), clamp_to)];
     }
   };
-  load_round(0, Lmax - 1);
   hv[0] = 0;  // before the history
   const int L = min(max(L_raw, 0), Lmax);
   const int last_tok = max(L - 1, 0);
-  int32_t sf[NM];  // sf[j] = h[L-1-j], the suffix
-#pragma unroll
-  for (int j = 0; j < NM; ++j) {
-    const int32_t x = h[max(L - 1 - j, 0)];
-    sf[j] = j < L ? x : 0;
-  }
+  const int32_t sx = h[max(L - 1 - min(lane, NM - 1), 0)];
+  __builtin_amdgcn_sched_barrier(0);
+  load_round(0, last_tok);
 #pragma unroll
   for (int pr = 1; pr < kNgPre; ++pr) {
     load_round(pr, last_tok);
@@ -102,6 +100,9 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
     cnt[t] = 0;
     last[t] = -1;
   }
+  int32_t sf[NM];  // sf[j] = h[L-1-j], the suffix
+#pragma unroll
+  for (int j = 0; j < NM; ++j) sf[j] = j < L ? __builtin_amdgcn_readlane(sx, j) : 0;
   const int jmax = min(n_max, L);  // the suffix has L tokens at most; n_max <= NM
   int c[NM], l[NM];  // per size n + 1: ends seen, the latest one (ends increase along a thread's walk)
 #pragma unroll
@@ -126,29 +127,48 @@ __global__ __launch_bounds__(kNgBlock) void k_ngram(const int32_t* hist, const i
     // h[e - 1], is the thread's own vr[r]
     uint32_t first = 0;
 #pragma unroll
-    for (int r = 0; r < kNgPer; ++r) {
-      const int e = base + ng_off<VEC4>(r, t);
-      first |= ((e < L && jmax > 0 && vr[r] == sf[0]) ? 1u : 0u) << r;
+    for (int r = 0; r < kNgPer; ++r) first |= (vr[r] == sf[0] ? 1u : 0u) << r;
+    // ends at or past L (the last round only; uniform test), or no suffix
+    if (base + kNgRound > L || jmax <= 0) {
+      uint32_t live = 0;
+#pragma unroll
+      for (int r = 0; r < kNgPer; ++r) live |= (base + ng_off<VEC4>(r, t) < L && jmax > 0 ? 1u : 0u) << r;
+      first &= live;
     }
     // size 1 straight from the bits (ends increase with r)
     c[0] += __popc(first);
     if (first) l[0] = base + ng_off<VEC4>(31 - __clz(first), t);
-    // longer sizes: only the ends whose last token matched, in increasing order
-    uint32_t more = NM > 1 ? first : 0u;
+    // size 2 likewise: the token before each end's last one, h[e - 2], is the
+    // thread's own vr[r - 1] within a vector, else the window's (end 1 has none)
+    uint32_t second = 0;
+    if (NM > 1 && jmax > 1) {  // uniform
+#pragma unroll
+      for (int r = 0; r < kNgPer; ++r) {
+        const int32_t pv = (VEC4 && (r & 3)) ? vr[r > 0 ? r - 1 : 0] : win[NM - 1 + ng_off<VEC4>(r, t)];
+        second |= (pv == sf[1] ? 1u : 0u) << r;
+      }
+      second &= first;
+      if (base == 1 && t == 0) second &= ~1u;
+      c[1] += __popc(second);
+      if (second) l[1] = base + ng_off<VEC4>(31 - __clz(second), t);
+    }
+    // longer sizes: only the ends whose last two tokens matched, in increasing order
+    uint32_t more = NM > 2 ? second : 0u;
     while (more) {
       const int r = __builtin_ctz(more);
       more &= more - 1u;
       const int e = base + ng_off<VEC4>(r, t);
       const int k = e - 1 - w0;
-      // match length m(e): trailing ones of the NM comparisons (j = 0 matched),
-      // cut to the sizes that exist (j < jmax and h[e-1-j] inside the history)
-      uint32_t bits = 1u;
+      // match length m(e): trailing ones of the NM comparisons (j = 0, 1
+      // matched), cut to the sizes that exist (j < jmax and h[e-1-j] inside
+      // the history)
+      uint32_t bits = 3u;
 #pragma unroll
-      for (int j = 1; j < NM; ++j) bits |= (win[k - j] == sf[j] ? 1u : 0u) << j;
+      for (int j = 2; j < NM; ++j) bits |= (win[k - j] == sf[j] ? 1u : 0u) << j;
       bits &= (1u << min(jmax, e)) - 1u;
       const int m = __builtin_ctz(~bits);
 #pragma unroll
-      for (int n = 1; n < NM; ++n) {
+      for (int n = 2; n < NM; ++n) {
         c[n] += m > n ? 1 : 0;
         l[n] = m > n ? e : l[n];
       }
