@@ -451,8 +451,12 @@ def main():
     n_host = n_acc.cpu().numpy()
     tok_host = tokens.cpu().numpy()
     kbs = kb_host if args.ragged else np.full(B, K)
-    rows_read, rows_needed = rows_per_step(n_host, kbs, K, greedy, args.full)
     rows_all = int(np.sum(kbs + 1)) if greedy else int(np.sum(2 * kbs + 1))
+    # one sweep of every row when asked for, or when the call's B (K + 1) +
+    # B K logit rows (B (K + 1) greedy) are below the library's rounds
+    # threshold (its default, 256 MiB)
+    full = args.full or (B * (K + 1 if greedy else 2 * K + 1) * V * elt < 256 * 2 ** 20)
+    rows_read, rows_needed = rows_per_step(n_host, kbs, K, greedy, full)
     swept, needed, swept_all = (r * V * elt for r in (rows_read, rows_needed, rows_all))
     reread = 0 if greedy else int(np.sum(np.where(n_host < kbs, 2, 1))) * V * elt
     step_s = wall / args.steps
@@ -493,7 +497,6 @@ def main():
     else:
         sweep_s = float(np.mean(sweep_ms)) / 1e3
         achieved = swept / sweep_s / 1e9
-        full = args.full or (swept_all * 1.0 < 256 * 2 ** 20)  # the library's rounds threshold (default)
         nr = 1 if full else len([b for b in ROUND_BEGINS if b <= K])
         kname = "k_sweep_lse" if not greedy else "k_sweep_argmax"
         line["roofline"] = {"bound": "hbm",
