@@ -267,6 +267,48 @@ int spec_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int3
 int spec_ngram_propose(const int32_t* history, const int32_t* lengths, int B, int L_max, int n_min, int n_max,
                        int min_hits, int K, int32_t* out_draft, int32_t* out_count, void* stream);
 
+/* Device-side input validation, a debugging aid.  While it is on, every
+ * spec_verify* call (spec_verify, _ex, _noalloc, _ragged, _ragged_ex) first
+ * runs one more pass over the inputs it uses and adds what it finds to
+ * counters kept on the current device, in this order:
+ *   SPECV_DBG_CALLS             calls validated
+ *   SPECV_DBG_BAD_DRAFT_IDS     draft ids outside [0, V) at positions 0 .. K_b - 1
+ *   SPECV_DBG_BAD_U_ACCEPT      accept uniforms outside (0, 1) (NaN included), same positions
+ *   SPECV_DBG_BAD_U_RESAMPLE    resample uniforms outside (0, 1)
+ *   SPECV_DBG_NAN_LOGITS        NaN logits in the rows the call reads
+ *   SPECV_DBG_INF_LOGITS        +inf logits in those rows
+ *   SPECV_DBG_ROWS_NO_FINITE    rows among them without a finite logit
+ * (the uniforms are counted in sampling mode only; the rows a call reads are
+ * target rows 0 .. K_b and draft rows 0 .. K_b - 1 of each sequence).  The
+ * verify step still runs on such inputs, with unspecified tokens and never an
+ * out-of-bounds access.  The pass reads every used logit once more, so it is
+ * for debugging, not for timing.  The environment variable SPECV_DEBUG=1,
+ * read at the first call, turns validation on; spec_debug_enable overrides it.
+ * The counters are per-device state of the library: calls on one device that
+ * overlap in time add to the same counters. */
+#define SPECV_DEBUG_COUNTERS      7
+#define SPECV_DBG_CALLS           0
+#define SPECV_DBG_BAD_DRAFT_IDS   1
+#define SPECV_DBG_BAD_U_ACCEPT    2
+#define SPECV_DBG_BAD_U_RESAMPLE  3
+#define SPECV_DBG_NAN_LOGITS      4
+#define SPECV_DBG_INF_LOGITS      5
+#define SPECV_DBG_ROWS_NO_FINITE  6
+
+/* Turn validation on (on != 0) or off for later calls; returns the previous
+ * setting (0 or 1). */
+int spec_debug_enable(int on);
+
+/* Copy the current device's first n counters (1 <= n <= SPECV_DEBUG_COUNTERS)
+ * to host memory `out`, after the device's work so far has finished (it
+ * synchronises the device).  Returns SPECV_OK, SPECV_E_NULL, SPECV_E_SHAPE (n
+ * out of range) or SPECV_E_HIP. */
+int spec_debug_counters(unsigned long long* out, int n);
+
+/* Zero the current device's counters (synchronising the device).  Returns
+ * SPECV_OK or SPECV_E_HIP. */
+int spec_debug_reset(void);
+
 /* Static description of a return code. */
 const char* spec_verify_strerror(int code);
 

@@ -24,11 +24,15 @@ FLAG_FP64, FLAG_ZW_ZERO, FLAG_BAD_DRAFT = 1, 2, 4
 ERRORS = {0: "SPECV_OK", -1: "SPECV_E_NULL", -2: "SPECV_E_SHAPE", -3: "SPECV_E_DTYPE", -4: "SPECV_E_TEMP",
           -5: "SPECV_E_WORKSPACE", -6: "SPECV_E_ALIGN", -7: "SPECV_E_HIP", -8: "SPECV_E_SCRATCH"}
 NOALLOC_SCRATCH = 32 << 20
+# device-side validation counters (spec_debug_counters), in this order
+DEBUG_COUNTERS = ("calls", "bad_draft_ids", "bad_u_accept", "bad_u_resample", "nan_logits", "inf_logits",
+                  "rows_no_finite")
 
 # every symbol include/specverify.h declares
 EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_noalloc", "spec_verify_ex",
            "spec_verify_ragged",
            "spec_verify_ragged_ex", "spec_verify_tree_workspace_size", "spec_verify_tree_greedy", "spec_tree_mask", "spec_ngram_propose",
+           "spec_debug_enable", "spec_debug_counters", "spec_debug_reset",
            "spec_verify_strerror", "spec_verify_version")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -75,6 +79,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_tree_mask.restype = i32
     lib.spec_ngram_propose.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.spec_ngram_propose.restype = i32
+    lib.spec_debug_enable.argtypes = [i32]
+    lib.spec_debug_enable.restype = i32
+    lib.spec_debug_counters.argtypes = [vp, i32]
+    lib.spec_debug_counters.restype = i32
+    lib.spec_debug_reset.argtypes = []
+    lib.spec_debug_reset.restype = i32
     lib.spec_verify_strerror.argtypes = [i32]
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     lib.spec_verify_version.argtypes = []
@@ -90,6 +100,28 @@ def strerror(code: int) -> str:
 
 def version() -> str:
     return load().spec_verify_version().decode()
+
+
+def debug_enable(on: bool) -> bool:
+    """Turn device-side input validation on or off for later verify calls;
+    returns the previous setting."""
+    return bool(load().spec_debug_enable(1 if on else 0))
+
+
+def debug_counters() -> dict:
+    """The current device's validation counters (synchronises the device)."""
+    buf = (ctypes.c_ulonglong * len(DEBUG_COUNTERS))()
+    rc = int(load().spec_debug_counters(ctypes.cast(buf, ctypes.c_void_p), len(DEBUG_COUNTERS)))
+    if rc != 0:
+        raise SpecVerifyError(rc, strerror(rc))
+    return dict(zip(DEBUG_COUNTERS, (int(v) for v in buf)))
+
+
+def debug_reset() -> None:
+    """Zero the current device's validation counters (synchronises the device)."""
+    rc = int(load().spec_debug_reset())
+    if rc != 0:
+        raise SpecVerifyError(rc, strerror(rc))
 
 
 def workspace_size(B: int, K: int, V: int, dtype: int, T: float) -> int:

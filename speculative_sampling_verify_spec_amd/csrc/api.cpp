@@ -291,6 +291,10 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   const bool timed = e0 && e1;
 
   P.kbs = reinterpret_cast<int32_t*>(ws + L.kbs);
+  if (debug_enabled_flag(nullptr)) {  // input validation, a debugging aid (see k_validate.hip)
+    unsigned long long* dbg = debug_counters_ptr();
+    if (!dbg || launch_validate(P, dtype, greedy, dbg, st) != hipSuccess) return SPECV_E_HIP;
+  }
   if (greedy) {
     if (launch_sweeps(P, dtype, true, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
       return SPECV_E_HIP;
@@ -486,6 +490,25 @@ int spec_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int3
   if (sv::launch_tree_mask(parents, B, N, out_mask, out_depth, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SPECV_E_HIP;
   return SPECV_OK;
+}
+
+int spec_debug_enable(int on) { return sv::debug_enabled_flag(&on) ? 1 : 0; }
+
+int spec_debug_counters(unsigned long long* out, int n) {
+  if (!out) return SPECV_E_NULL;
+  if (n < 1 || n > SPECV_DEBUG_COUNTERS) return SPECV_E_SHAPE;
+  unsigned long long* d = sv::debug_counters_ptr();
+  if (!d || hipDeviceSynchronize() != hipSuccess) return SPECV_E_HIP;
+  return hipMemcpy(out, d, static_cast<size_t>(n) * sizeof(unsigned long long), hipMemcpyDeviceToHost) == hipSuccess
+             ? SPECV_OK
+             : SPECV_E_HIP;
+}
+
+int spec_debug_reset(void) {
+  unsigned long long* d = sv::debug_counters_ptr();
+  if (!d || hipDeviceSynchronize() != hipSuccess) return SPECV_E_HIP;
+  const unsigned long long zero[SPECV_DEBUG_COUNTERS] = {};
+  return hipMemcpy(d, zero, sizeof zero, hipMemcpyHostToDevice) == hipSuccess ? SPECV_OK : SPECV_E_HIP;
 }
 
 const char* spec_verify_strerror(int code) {

@@ -183,6 +183,11 @@ hipError_t launch_exact(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_greedy_scan(const Params& p, hipStream_t s);
 hipError_t launch_round_accept(const Params& p, int dtype, bool greedy, hipStream_t s);
 hipError_t launch_position_stats(const Params& p, hipStream_t s);
+hipError_t launch_validate(const Params& p, int dtype, bool greedy, unsigned long long* dbg, hipStream_t s);
+// whether validation is on (read from SPECV_DEBUG at the first use); with
+// set_to, sets it and returns the previous value
+bool debug_enabled_flag(int* set_to);
+unsigned long long* debug_counters_ptr();  // the current device's counters, or null
 hipError_t launch_tree_scan(const Params& p, hipStream_t s);
 hipError_t launch_ngram(const int32_t* hist, const int32_t* lengths, int B, int Lmax, int n_min, int n_max,
                         int min_hits, int K, int32_t* out_draft, int32_t* out_count, hipStream_t s);

@@ -22,6 +22,9 @@ sigs = {
     "spec_ngram_propose": ([vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp], i32),
     "spec_verify_strerror": ([i32], ctypes.c_char_p),
     "spec_verify_version": ([], ctypes.c_char_p),
+    "spec_debug_enable": ([i32], i32),
+    "spec_debug_counters": ([vp, i32], i32),
+    "spec_debug_reset": ([], i32),
 }
 for name, (args, res) in sigs.items():
     f = getattr(lib, name)
@@ -84,6 +87,18 @@ assert lib.spec_tree_mask(PA, 4, 65, OTT, OP, None) == -2
 assert lib.spec_tree_mask(PA, 4, 16, OTT, OP, None) == -7
 assert lib.spec_ngram_propose(L, TT, 4, 100, 3, 2, 1, 5, OTT, OP, None) == -2
 assert lib.spec_ngram_propose(L, TT, 4, 100, 1, 4, 1, 5, OTT, OP, None) == -7
+# device-side validation: argument checks, the HIP errors of the stand-ins,
+# and a verify call with validation on (its validation launch fails first)
+CNT = (ctypes.c_ulonglong * 8)()
+assert lib.spec_debug_counters(None, 1) == -1
+assert lib.spec_debug_counters(ctypes.cast(CNT, vp), 0) == -2
+assert lib.spec_debug_counters(ctypes.cast(CNT, vp), 8) == -2
+assert lib.spec_debug_counters(ctypes.cast(CNT, vp), 7) == -7
+assert lib.spec_debug_reset() == -7
+assert lib.spec_debug_enable(1) == 0
+assert lib.spec_verify(P, Q, X, UA, UR, 1.0, 4, 3, 128, OT, ON, F32, WS, BIG, None) == -7
+assert lib.spec_verify(P, Q, X, UA, UR, 1.0, 0, 3, 128, OT, ON, F32, WS, BIG, None) == -2
+assert lib.spec_debug_enable(0) == 1
 for code in range(-9, 1):
     assert lib.spec_verify_strerror(code)
 assert b"gfx950" in lib.spec_verify_version()

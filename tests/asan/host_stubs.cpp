@@ -1,7 +1,8 @@
 // Host-only stand-ins for a CPU AddressSanitizer build of api.cpp: the
-// kernel launchers and the three HIP runtime calls api.cpp makes.  Every
-// launcher reports a launch failure, so a call that passes the host-side
-// checks returns SPECV_E_HIP; no device is ever touched.
+// kernel launchers, the validation hooks and the HIP runtime calls api.cpp
+// makes.  Every launcher and runtime call reports a failure, so a call that
+// passes the host-side checks returns SPECV_E_HIP; no device is ever touched.
+#include "specverify.h"
 #include "sv_internal.h"
 
 namespace sv {
@@ -18,6 +19,17 @@ hipError_t launch_ngram(const int32_t*, const int32_t*, int, int, int, int, int,
   return hipErrorInvalidValue;
 }
 hipError_t launch_tree_mask(const int32_t*, int, int, uint8_t*, int32_t*, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_validate(const Params&, int, bool, unsigned long long*, hipStream_t) { return hipErrorInvalidValue; }
+bool debug_enabled_flag(int* set_to) {
+  static int on = 0;
+  const bool prev = on != 0;
+  if (set_to) on = *set_to ? 1 : 0;
+  return prev;
+}
+unsigned long long* debug_counters_ptr() {  // a device array's address (none here)
+  static unsigned long long counters[SPECV_DEBUG_COUNTERS];
+  return counters;
+}
 }  // namespace sv
 
 extern "C" {
@@ -33,4 +45,6 @@ hipError_t hipGetSymbolAddress(void** ptr, const void*) {
   *ptr = nullptr;
   return hipErrorInvalidSymbol;
 }
+hipError_t hipDeviceSynchronize(void) { return hipErrorInvalidValue; }
+hipError_t hipMemcpy(void*, const void*, size_t, hipMemcpyKind) { return hipErrorInvalidValue; }
 }

@@ -35,6 +35,9 @@ def test_header_constants_match_binding():
     assert consts["SPECV_MAX_NGRAM"] == sv.SPECV_MAX_NGRAM
     assert consts["SPECV_FLAG_ZW_ZERO"] == sv.FLAG_ZW_ZERO and consts["SPECV_FLAG_BAD_DRAFT"] == sv.FLAG_BAD_DRAFT
     assert consts["SPECV_FLAG_FP64"] == sv.FLAG_FP64
+    assert consts["SPECV_DEBUG_COUNTERS"] == len(sv.DEBUG_COUNTERS)
+    for i, name in enumerate(sv.DEBUG_COUNTERS):
+        assert consts["SPECV_DBG_" + name.upper()] == i, name
     for code, name in sv.ERRORS.items():
         assert consts.get(name, 0) == code, name
 
@@ -204,3 +207,17 @@ def test_noalloc_scratch_size_matches_header():
     m = re.search(r"#define\s+SPECV_NOALLOC_SCRATCH\s+\((\d+)u\s*<<\s*(\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == sv.NOALLOC_SCRATCH
     assert "SPECV_E_SCRATCH" in sv.ERRORS.values()
+
+
+def test_debug_counter_checks(lib):
+    """spec_debug_counters rejects a NULL destination and a count out of
+    [1, SPECV_DEBUG_COUNTERS] before any HIP call; spec_debug_enable reports
+    the previous setting."""
+    import ctypes
+    buf = (ctypes.c_ulonglong * 8)()
+    assert lib.spec_debug_counters(None, 1) == -1
+    assert lib.spec_debug_counters(ctypes.cast(buf, ctypes.c_void_p), 0) == -2
+    assert lib.spec_debug_counters(ctypes.cast(buf, ctypes.c_void_p), len(sv.DEBUG_COUNTERS) + 1) == -2
+    prev = lib.spec_debug_enable(1)
+    assert lib.spec_debug_enable(0) == 1
+    assert lib.spec_debug_enable(prev) == 0
