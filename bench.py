@@ -17,10 +17,13 @@ over about the first second; the steps it took are reported (`ramp_steps`).
 Prints one JSON line.  `value` and `ms_per_step` come from a first timed
 pass of K steps with nothing else in the stream.  A second timed pass of K
 steps records events between steps (`step_us`: median, p10, p90, first and
-last step) and, with the sweep's dispatches, events that time the sweep
-alone (`sweep_us`); those cost the step some microseconds, so that pass's
-mean is reported separately (`ms_per_step_with_events`).  `roofline`
-describes the dominant kernel (the row sweep) from those sweep events.
+last step) and, with each of the sweep's dispatches, events that time every
+sweep launch on its own (spec_verify_sweep_timed): `sweep_us` is the sweep
+phase (first sweep launch's start to the last one's end, the acceptance
+launches between rounds included) and `sweep_launches_us` the sweep launches
+alone; those events cost the step some microseconds, so that pass's mean is
+reported separately (`ms_per_step_with_events`).  `roofline` describes the
+dominant kernel, the row sweep, from its launches' own durations.
 `cpu_baseline` times the fp64 oracle on the same batch on all host threads
 and on one.
 
@@ -89,6 +92,12 @@ class HipEvents:
             a, b = ctypes.c_void_p(), ctypes.c_void_p()
             assert self.hip.hipEventCreate(ctypes.byref(a)) == 0 and self.hip.hipEventCreate(ctypes.byref(b)) == 0
             self.pairs.append((a.value, b.value))
+
+    def between_ms(self, a: int, b: int) -> float:
+        """From the start event of pair a to the end event of pair b."""
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), self.pairs[a][0], self.pairs[b][1]) == 0
+        return ms.value
 
     def elapsed_ms(self, i: int) -> float:
         ms = ctypes.c_float()
@@ -390,7 +399,9 @@ def main():
     n_acc = torch.empty((B,), dtype=torch.int32, device="cuda")
     flags = torch.empty((B,), dtype=torch.int32, device="cuda")
     logz = torch.empty((B, 2 * K + 1), dtype=torch.float32, device="cuda") if args.full else None
-    ev = HipEvents(args.steps)
+    nev = len(ROUND_BEGINS)  # sweep launches per call, at most
+    ev = HipEvents(args.steps * nev)
+    nsweeps = []
 
     kb_host = workloads.ragged_draft_counts(B, K) if args.ragged else None
     if args.ragged:
@@ -419,9 +430,12 @@ def main():
         turn[0] += 1
         if e is None:
             rc = call()
-        else:  # events change every step
-            rc = sv.spec_verify(cp, cq, x, ua, ur, T, tokens, n_acc, ws, out_flags=flags, out_logz=logz, events=e,
-                                extended=True)
+        else:  # step e of the events pass: a pair of events per sweep launch
+            pairs = ev.pairs[e * nev:(e + 1) * nev]
+            rc, ns = sv.spec_verify_sweep_timed(cp, cq, x, ua, ur, T, tokens, n_acc, ws,
+                                                [a for a, _ in pairs], [b for _, b in pairs],
+                                                out_logz=logz, out_flags=flags)
+            nsweeps.append(ns)
         if rc != 0:
             raise RuntimeError(sv.strerror(rc))
 
@@ -440,12 +454,15 @@ def main():
     t0 = time.perf_counter()
     bounds[0].record()
     for i in range(args.steps):
-        step(None if args.ragged else ev.pairs[i])
+        step(None if args.ragged else i)
         bounds[i + 1].record()
     torch.cuda.synchronize()
     wall_ev = time.perf_counter() - t0
     step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]
-    sweep_ms = None if args.ragged else [ev.elapsed_ms(i) for i in range(args.steps)]
+    # per step: the sweep phase, and the sweep launches' own durations summed
+    sweep_ms = None if args.ragged else [ev.between_ms(i * nev, i * nev + nsweeps[i] - 1) for i in range(args.steps)]
+    launches_ms = None if args.ragged else [sum(ev.elapsed_ms(i * nev + r) for r in range(nsweeps[i]))
+                                            for i in range(args.steps)]
     ev.close()
 
     n_host = n_acc.cpu().numpy()
@@ -470,6 +487,7 @@ def main():
         "ramp_steps": ramp_steps, "ramp_seconds": round(ramp_s, 3),
         "step_us": dist_us(step_ms),
         "sweep_us": None if sweep_ms is None else dist_us(sweep_ms),
+        "sweep_launches_us": None if launches_ms is None else dist_us(launches_ms),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{wl.name}: verify {batch.wl.describe()}, logits {batch.dtype}"
@@ -495,24 +513,32 @@ def main():
     if args.ragged:
         line["position_stats"] = stats.cpu().numpy().tolist()
     else:
-        sweep_s = float(np.mean(sweep_ms)) / 1e3
-        achieved = swept / sweep_s / 1e9
-        nr = 1 if full else len([b for b in ROUND_BEGINS if b <= K])
+        nr = nsweeps[0]
+        assert all(n == nr for n in nsweeps), nsweeps
+        assert nr == (1 if full else len([b for b in ROUND_BEGINS if b <= K])), nr
+        launches_s = float(np.mean(launches_ms)) / 1e3  # the sweep launches of one step, summed
+        phase_s = float(np.mean(sweep_ms)) / 1e3
+        achieved = swept / launches_s / 1e9
         kname = "k_sweep_lse" if not greedy else "k_sweep_argmax"
         line["roofline"] = {"bound": "hbm",
-                            "kernel": f"row sweep: {kname}" if nr == 1 else
-                                      f"row sweep: {nr} round launches of {kname} and {nr - 1} of k_round_accept "
-                                      "between them, timed together (first sweep dispatch start to last end)",
+                            "kernel": f"row sweep: {kname}, " + ("one launch per step" if nr == 1 else
+                                      f"{nr} round launches per step, each timed with HIP events recorded "
+                                      "with its own dispatch"),
                             "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": achieved / PEAK_HBM_GBS,
                             # the committed counters cover the headline's log-sum-exp sweep
                             "traffic": None if (greedy or args.full or args.seqs or args.workload != HEADLINE)
                             else counter_traffic(swept),
-                            "launch_us": sweep_s * 1e6, "launches_timed": args.steps,
+                            "launch_us": launches_s / nr * 1e6, "launches_timed": args.steps * nr,
                             "sweep_launches_per_step": nr,
-                            "algorithmic_bytes_per_launch": swept,
+                            "algorithmic_bytes_per_launch": swept / nr,
                             "algorithmic_bytes": "the logit rows the sweep reads (rows of the positions each "
-                                                 "sequence reached), V * element size each"}
+                                                 "sequence reached), V * element size each; per launch, the "
+                                                 "step's rows over its launches",
+                            # the sweep phase: first sweep launch's start to the last one's end, with the
+                            # acceptance launches between the rounds
+                            "sweep_phase_us": phase_s * 1e6,
+                            "sweep_phase_frac": swept / phase_s / 1e9 / PEAK_HBM_GBS}
     if not args.no_cpu_baseline:
         log(f"timing the fp64 oracle on a sample (~{args.cpu_seconds:.0f}s)")
         line["cpu_baseline"] = cpu_baseline(batch, tok_host, n_host, args.cpu_seconds)

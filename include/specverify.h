@@ -163,6 +163,22 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
                    void* workspace, size_t workspace_bytes, void* stream,
                    float* out_logz, int32_t* out_flags, void* ev_sweep_begin, void* ev_sweep_end);
 
+/* spec_verify_ex with every row-sweep launch of the call timed on its own,
+ * for a benchmark's per-kernel roofline.  ev_begin[i] and ev_end[i]
+ * (hipEvent_t handles, as void*) are recorded with the start and the end of
+ * the call's i-th sweep launch (one launch when every row is swept at once,
+ * up to three when the rows are read in rounds); launches from n_events on
+ * are not timed, and the acceptance launches between rounds lie outside every
+ * pair.  *n_sweeps (host memory, or NULL) receives the number of sweep
+ * launches.  Returns what spec_verify_ex returns, or SPECV_E_SHAPE for
+ * n_events < 0 and SPECV_E_NULL when n_events > 0 and an event array is NULL. */
+int spec_verify_sweep_timed(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
+                            const float* u_accept, const float* u_resample, float T, int B, int K, int V,
+                            int32_t* out_tokens, int32_t* out_n_accepted, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            float* out_logz, int32_t* out_flags, void* const* ev_begin, void* const* ev_end,
+                            int n_events, int* n_sweeps);
+
 /*
  * spec_verify_ragged - spec_verify with a draft count per sequence, and
  * optional per-position acceptance counters.

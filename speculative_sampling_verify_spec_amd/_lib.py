@@ -30,6 +30,7 @@ DEBUG_COUNTERS = ("calls", "bad_draft_ids", "bad_u_accept", "bad_u_resample", "n
 
 # every symbol include/specverify.h declares
 EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_noalloc", "spec_verify_ex",
+           "spec_verify_sweep_timed",
            "spec_verify_ragged",
            "spec_verify_ragged_ex", "spec_verify_tree_workspace_size", "spec_verify_tree_greedy", "spec_tree_mask", "spec_ngram_propose",
            "spec_debug_enable", "spec_debug_counters", "spec_debug_reset",
@@ -66,6 +67,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_verify_noalloc.restype = i32
     lib.spec_verify_ex.argtypes = common + [vp, vp, vp, vp]
     lib.spec_verify_ex.restype = i32
+    lib.spec_verify_sweep_timed.argtypes = common + [vp, vp, vp, vp, i32, vp]
+    lib.spec_verify_sweep_timed.restype = i32
     ragged = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp]
     lib.spec_verify_ragged.argtypes = ragged
     lib.spec_verify_ragged.restype = i32
@@ -183,6 +186,25 @@ def bind_spec_verify(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: 
     place)."""
     return _bound(*_spec_verify_call(logits_p, logits_q, draft_tokens, u_accept, u_resample, T, out_tokens,
                                      out_n_accepted, workspace, out_logz, out_flags, None, stream, extended))
+
+
+def spec_verify_sweep_timed(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, out_tokens,
+                            out_n_accepted, workspace, ev_begin, ev_end, out_logz=None, out_flags=None,
+                            stream=None):
+    """spec_verify_sweep_timed on torch device tensors: ev_begin, ev_end are
+    sequences of hipEvent_t handles (ints), recorded with each sweep launch in
+    turn.  Returns (return code, number of sweep launches)."""
+    n = len(ev_begin)
+    if len(ev_end) != n:
+        raise ValueError("ev_begin and ev_end need the same length")
+    beg = (ctypes.c_void_p * max(n, 1))(*ev_begin)
+    end = (ctypes.c_void_p * max(n, 1))(*ev_end)
+    ns = ctypes.c_int(0)
+    _, args = _spec_verify_call(logits_p, logits_q, draft_tokens, u_accept, u_resample, T, out_tokens,
+                                out_n_accepted, workspace, out_logz, out_flags, None, stream, True)
+    args = args[:-2] + [ctypes.cast(beg, ctypes.c_void_p), ctypes.cast(end, ctypes.c_void_p), n, ctypes.byref(ns)]
+    rc = int(load().spec_verify_sweep_timed(*args))
+    return rc, int(ns.value)
 
 
 def spec_verify_noalloc(logits_p, logits_q, draft_tokens, u_accept, u_resample, T: float, out_tokens,

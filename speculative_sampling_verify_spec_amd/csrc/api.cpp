@@ -167,22 +167,38 @@ int last_round_begin(int K) {
   return b;
 }
 
+// Events recorded with each sweep launch (spec_verify_sweep_timed): launch r
+// < n starts with begin[r] and ends with end[r]; `launches` receives the
+// number of sweep launches of the call.
+struct SweepTiming {
+  const hipEvent_t* begin;
+  const hipEvent_t* end;
+  int n;
+  int launches;
+};
+
 // The sweep's launches for one call: every row at once when `full`, else
-// rounds of levels (see round_begin) with k_round_accept between them; the
-// events go to the first and the last sweep launch.
-hipError_t launch_sweeps(Params P, int dtype, bool greedy, bool full, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+// rounds of levels (see round_begin) with k_round_accept between them.  The
+// events e0 and e1 go to the first and the last sweep launch; with `tm`,
+// each launch gets its own pair instead.
+hipError_t launch_sweeps(Params P, int dtype, bool greedy, bool full, hipStream_t st, hipEvent_t e0, hipEvent_t e1,
+                         SweepTiming* tm = nullptr) {
   auto launch = [&](const Params& q, hipEvent_t a, hipEvent_t b) {
     return greedy ? launch_sweep_argmax(q, dtype, st, a, b) : launch_sweep_lse(q, dtype, st, a, b);
   };
+  auto begin_ev = [&](int r) { return tm ? (r < tm->n ? tm->begin[r] : nullptr) : (r == 0 ? e0 : nullptr); };
+  auto end_ev = [&](int r, int nr) { return tm ? (r < tm->n ? tm->end[r] : nullptr) : (r == nr - 1 ? e1 : nullptr); };
   if (full) {
     P.grid3 = P.kb ? 1 : 0;  // per-sequence counts need the 3-D grid
     P.lv0 = 0;
     P.lv1 = P.K + 1;
-    return launch(P, e0, e1);
+    if (tm) tm->launches = 1;
+    return launch(P, begin_ev(0), end_ev(0, 1));
   }
   int bounds[kMaxRounds + 1], nr = 0;
   for (int r = 0; r < kMaxRounds && round_begin(r) <= P.K; ++r) bounds[nr++] = round_begin(r);
   bounds[nr] = P.K + 1;
+  if (tm) tm->launches = nr;
   P.grid3 = 1;
   for (int r = 0; r < nr; ++r) {
     if (r > 0) {  // the tests of the round just swept
@@ -194,7 +210,7 @@ hipError_t launch_sweeps(Params P, int dtype, bool greedy, bool full, hipStream_
     }
     P.lv0 = bounds[r];
     P.lv1 = bounds[r + 1];
-    const hipError_t rc = launch(P, r == 0 ? e0 : nullptr, r == nr - 1 ? e1 : nullptr);
+    const hipError_t rc = launch(P, begin_ev(r), end_ev(r, nr));
     if (rc != hipSuccess) return rc;
   }
   return hipSuccess;
@@ -240,7 +256,7 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
                 const float* u_accept, const float* u_resample, float T, int B, int K, int V,
                 int32_t* out_tokens, int32_t* out_n_accepted, unsigned long long* position_stats, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream, float* out_logz, int32_t* out_flags,
-                void* ev_sweep_begin, void* ev_sweep_end, size_t* need = nullptr) {
+                void* ev_sweep_begin, void* ev_sweep_end, size_t* need = nullptr, SweepTiming* tm = nullptr) {
   if (dtype != SPECV_F32 && dtype != SPECV_BF16) return SPECV_E_DTYPE;
   if (!valid_temperature(T)) return SPECV_E_TEMP;
   const bool greedy = T == 0.f;
@@ -296,7 +312,7 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
     if (!dbg || launch_validate(P, dtype, greedy, dbg, st) != hipSuccess) return SPECV_E_HIP;
   }
   if (greedy) {
-    if (launch_sweeps(P, dtype, true, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
+    if (launch_sweeps(P, dtype, true, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr, tm) != hipSuccess)
       return SPECV_E_HIP;
     if (launch_greedy_scan(P, st) != hipSuccess) return SPECV_E_HIP;
     if (position_stats && launch_position_stats(P, st) != hipSuccess) return SPECV_E_HIP;
@@ -319,7 +335,7 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   P.spq = reinterpret_cast<double*>(ws + L.spq);
   P.vcount = reinterpret_cast<uint32_t*>(ws + L.vcount);
 
-  if (launch_sweeps(P, dtype, false, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr) != hipSuccess)
+  if (launch_sweeps(P, dtype, false, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr, tm) != hipSuccess)
     return SPECV_E_HIP;
   P.vpre = full ? 0 : last_round_begin(K);
   // more sequences than CUs: two smaller workgroups per CU (see launch_verify)
@@ -359,6 +375,24 @@ int spec_verify_ex(const void* logits_p, const void* logits_q, const int32_t* dr
   return sv::verify_impl(logits_p, logits_q, draft_tokens, nullptr, u_accept, u_resample, T, B, K, V, out_tokens,
                          out_n_accepted, nullptr, dtype, workspace, workspace_bytes, stream, out_logz, out_flags,
                          ev_sweep_begin, ev_sweep_end);
+}
+
+int spec_verify_sweep_timed(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,
+                            const float* u_accept, const float* u_resample, float T, int B, int K, int V,
+                            int32_t* out_tokens, int32_t* out_n_accepted, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            float* out_logz, int32_t* out_flags, void* const* ev_begin, void* const* ev_end,
+                            int n_events, int* n_sweeps) {
+  if (n_sweeps) *n_sweeps = 0;
+  if (n_events < 0) return SPECV_E_SHAPE;
+  if (n_events > 0 && (!ev_begin || !ev_end)) return SPECV_E_NULL;
+  sv::SweepTiming tm{reinterpret_cast<const hipEvent_t*>(ev_begin), reinterpret_cast<const hipEvent_t*>(ev_end),
+                     n_events, 0};
+  const int rc = sv::verify_impl(logits_p, logits_q, draft_tokens, nullptr, u_accept, u_resample, T, B, K, V,
+                                 out_tokens, out_n_accepted, nullptr, dtype, workspace, workspace_bytes, stream,
+                                 out_logz, out_flags, nullptr, nullptr, nullptr, &tm);
+  if (n_sweeps) *n_sweeps = tm.launches;
+  return rc;
 }
 
 int spec_verify_noalloc(const void* logits_p, const void* logits_q, const int32_t* draft_tokens,

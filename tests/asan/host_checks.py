@@ -14,6 +14,7 @@ sigs = {
     "spec_verify": (common, i32),
     "spec_verify_ex": (common + [vp] * 4, i32),
     "spec_verify_noalloc": (common[:12] + [vp], i32),
+    "spec_verify_sweep_timed": (common + [vp] * 4 + [i32, vp], i32),
     "spec_verify_ragged": ([vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp], i32),
     "spec_verify_ragged_ex": ([vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, vp, vp, vp, i32, vp, sz, vp, vp, vp], i32),
     "spec_verify_tree_workspace_size": ([i32] * 4, sz),
@@ -87,6 +88,20 @@ assert lib.spec_tree_mask(PA, 4, 65, OTT, OP, None) == -2
 assert lib.spec_tree_mask(PA, 4, 16, OTT, OP, None) == -7
 assert lib.spec_ngram_propose(L, TT, 4, 100, 3, 2, 1, 5, OTT, OP, None) == -2
 assert lib.spec_ngram_propose(L, TT, 4, 100, 1, 4, 1, 5, OTT, OP, None) == -7
+# per-launch sweep timing: its own checks, then the common ones; the number
+# of launches is written on every return
+NS = ctypes.c_int(7)
+EVB = (vp * 3)(0x100, 0x200, 0x300)
+EVE = (vp * 3)(0x101, 0x201, 0x301)
+T3 = (P, Q, X, UA, UR, 1.0, 4, 3, 128, OT, ON, F32, WS, BIG, None, None, None)
+assert lib.spec_verify_sweep_timed(*T3, ctypes.cast(EVB, vp), ctypes.cast(EVE, vp), -1, ctypes.byref(NS)) == -2
+assert NS.value == 0
+assert lib.spec_verify_sweep_timed(*T3, None, ctypes.cast(EVE, vp), 3, ctypes.byref(NS)) == -1
+assert lib.spec_verify_sweep_timed(*T3[:4], None, *T3[5:], ctypes.cast(EVB, vp), ctypes.cast(EVE, vp), 3,
+                                   ctypes.byref(NS)) == -1
+assert lib.spec_verify_sweep_timed(*T3, ctypes.cast(EVB, vp), ctypes.cast(EVE, vp), 3, None) == -7
+assert lib.spec_verify_sweep_timed(*T3, None, None, 0, ctypes.byref(NS)) == -7
+
 # device-side validation: argument checks, the HIP errors of the stand-ins,
 # and a verify call with validation on (its validation launch fails first)
 CNT = (ctypes.c_ulonglong * 8)()
