@@ -160,6 +160,23 @@ double rounds_min_bytes() {
   return v;
 }
 
+// Largest batch that takes the one-launch path for short rows (k_short):
+// kShortSeqsPerCU sequences per CU, or SPECV_SHORT_MAX_SEQS from the
+// environment (read once per process; 0 turns the path off).
+int short_max_seqs() {
+  static std::once_flag once;
+  static long v = -1;
+  std::call_once(once, [] {
+    const char* e = std::getenv("SPECV_SHORT_MAX_SEQS");
+    if (e && *e) {
+      char* end = nullptr;
+      const long d = std::strtol(e, &end, 10);
+      if (end != e && d >= 0) v = d;
+    }
+  });
+  return v >= 0 ? static_cast<int>(std::min(v, 1L << 30)) : kShortSeqsPerCU * device_cus();
+}
+
 // The first level of the last round for K drafts.
 int last_round_begin(int K) {
   int b = 0;
@@ -335,6 +352,18 @@ int verify_impl(const void* logits_p, const void* logits_q, const int32_t* draft
   P.spq = reinterpret_cast<double*>(ws + L.spq);
   P.vcount = reinterpret_cast<uint32_t*>(ws + L.vcount);
 
+  if (P.R3 <= kSoloMaxChunks && V <= kShortMaxV && B <= short_max_seqs()) {
+    // short rows: the whole step in one launch, which carries the sweep's events
+    hipEvent_t a = timed ? e0 : nullptr, b = timed ? e1 : nullptr;
+    if (tm) {
+      a = tm->n > 0 ? tm->begin[0] : nullptr;
+      b = tm->n > 0 ? tm->end[0] : nullptr;
+      tm->launches = 1;
+    }
+    if (launch_short(P, dtype, st, a, b) != hipSuccess) return SPECV_E_HIP;
+    if (position_stats && launch_position_stats(P, st) != hipSuccess) return SPECV_E_HIP;
+    return SPECV_OK;
+  }
   if (launch_sweeps(P, dtype, false, full, st, timed ? e0 : nullptr, timed ? e1 : nullptr, tm) != hipSuccess)
     return SPECV_E_HIP;
   P.vpre = full ? 0 : last_round_begin(K);

@@ -14,6 +14,13 @@ constexpr int kMaxDrawChunks = 256;   // fp64 draw chunks per row: one wave comb
 constexpr int kXBlock = 128;          // threads that compute one fp64 draw chunk's sums
 constexpr int kSoloMaxChunks = 2;     // rows of at most this many fp64 draw chunks: one fp64 launch (k_exact_solo)
 constexpr int kEagerMaxRounds = 4;    // k_verify's chunk-sum workgroups: at most this many chunks per group of 128 threads
+// Rows of at most kShortMaxV tokens (two fp64 draw chunks of 1024) in batches
+// of at most kShortSeqsPerCU sequences per CU (or SPECV_SHORT_MAX_SEQS) take
+// one launch for the whole step in sampling mode (k_short).  Measured at
+// K = 4, V = 1000 fp32 (us per call, one launch against the general path):
+// B = 1 8.2 / 11.4, B = 256 9.2 / 22.7, B = 2048 58.2 / 65.2.
+constexpr int kShortMaxV = kSoloMaxChunks * 1024;
+constexpr int kShortSeqsPerCU = 8;
 
 // Elements one lane of a row sweep holds: 16-byte units on the vector path,
 // sixteen single elements on the scalar path.  The vector path has two
@@ -180,6 +187,7 @@ hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t s, hipEvent_
 hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_verify(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_exact(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_short(const Params& p, int dtype, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_greedy_scan(const Params& p, hipStream_t s);
 hipError_t launch_round_accept(const Params& p, int dtype, bool greedy, hipStream_t s);
 hipError_t launch_position_stats(const Params& p, hipStream_t s);

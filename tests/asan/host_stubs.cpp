@@ -10,6 +10,7 @@ hipError_t launch_sweep_lse(const Params&, int, hipStream_t, hipEvent_t, hipEven
 hipError_t launch_sweep_argmax(const Params&, int, hipStream_t, hipEvent_t, hipEvent_t) { return hipErrorInvalidValue; }
 hipError_t launch_verify(const Params&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_exact(const Params&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_short(const Params&, int, hipStream_t, hipEvent_t, hipEvent_t) { return hipErrorInvalidValue; }
 hipError_t launch_greedy_scan(const Params&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_round_accept(const Params&, int, bool, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_position_stats(const Params&, hipStream_t) { return hipErrorInvalidValue; }

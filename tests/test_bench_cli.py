@@ -17,7 +17,7 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
-def test_seqs_beyond_the_workload_is_refused():
-    r = run("--workload", "1", "--seqs", "65")
+def test_negative_seqs_is_refused():
+    r = run("--workload", "1", "--seqs", "-1")
     assert r.returncode == 2
     assert "--seqs" in r.stderr

@@ -46,8 +46,9 @@ def edge_uniforms(b, ref, lo_min=1e-3, margin_lo=1e-11, margin_hi=1e-7):
     return ur, np.array(chosen, dtype=np.int64), np.array(tokens, dtype=np.int64)
 
 
-# V = 999, 1000 and 2000: rows of one and two fp64 chunks, drawn by the
-# one-launch kernel (V = 999: element loads, not 16-byte vectors)
+# V = 999, 1000 and 2000: rows of one and two fp64 chunks; batches of at most
+# one sequence per CU take the one-launch path for short rows, which draws
+# every token in fp64 (V = 999: element loads, not 16-byte vectors)
 @pytest.mark.parametrize("cfg,nseq,V", [(1, None, None), (2, 32, None), (3, 16, None), (1, 48, 1000), (0, 40, 2000),
                                         (1, 24, 999)],
                          ids=["small-bf16", "headline-bf16", "sharp-fp32", "V1000-bf16", "V2000-fp32",
@@ -104,3 +105,38 @@ def test_sums_ahead_match_the_queued_path(gpu_lib, cfg, V):
     np.testing.assert_array_equal(g.n, big.n[:64])
     np.testing.assert_array_equal(g.flags, big.flags[:64])
     compare(small, g, oracle.verify_batch(small)).check()
+
+
+def _cus():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("cfg,V", [(1, 1000), (0, 2000), (1, 999)], ids=["V1000-bf16", "V2000-fp32", "V999-bf16-scalar"])
+def test_short_rows_both_paths(gpu_lib, cfg, V):
+    """Short rows (at most two fp64 chunks) are drawn by the one-launch kernel
+    in batches of at most eight sequences per CU, and by the sweep, k_verify
+    and the one-workgroup fp64 kernel in larger ones.  The same 64 sequences,
+    with edge uniforms, alone and at the head of a batch of 8 CUs + 64: both
+    meet the oracle's parity rule, every edge draw is an fp64 draw on both
+    paths, and the two agree wherever their counts do."""
+    B = 8 * _cus() + 64
+    b = workloads.make_batch(cfg, seqs=range(B), workers=workloads.default_workers(), V=V)
+    ref = oracle.verify_batch(b, workers=workloads.default_workers())
+    ur, chosen, _ = edge_uniforms(b, ref)
+    b2 = dataclasses.replace(b, u_resample=ur)
+    ref2 = oracle.verify_batch(b2, workers=workloads.default_workers())
+    print(f"cfg {cfg} V={b.V}: {B} sequences, {len(chosen)} edge uniforms", flush=True)
+    big = run_gpu(gpu_lib, b2)
+    compare(b2, big, ref2).check()
+    small = _head(b2, 64)
+    g = run_gpu(gpu_lib, small)
+    compare(small, g, oracle.verify_batch(small)).check()
+    c64 = chosen[chosen < 64]
+    assert len(c64) >= 16
+    assert np.all(g.flags & sv.FLAG_FP64), "the one-launch path draws every token in fp64"
+    assert np.all(big.flags[c64] & sv.FLAG_FP64), "an edge draw was certified by the fp32 path"
+    same = g.n == big.n[:64]
+    assert same.sum() >= 60
+    np.testing.assert_array_equal(g.tokens[same], big.tokens[:64][same])
+    np.testing.assert_array_equal(g.flags & ~sv.FLAG_FP64, big.flags[:64] & ~sv.FLAG_FP64)
