@@ -63,7 +63,10 @@ typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype_t;
  * cannot see another's published sums after a short bounded wait hands the
  * draw to the fp64 path, so in principle this bit may differ between two
  * identical calls.  The tokens, the counts and the other bits never do (the
- * fp64 path draws the same token wherever the fast one is certified). */
+ * fp64 path draws the same token wherever the fast one is certified).  Rows
+ * of at most 2048 tokens in batches of at most eight sequences per compute
+ * unit take one launch that draws every token in fp64: there the bit is set
+ * on every sequence. */
 #define SPECV_FLAG_FP64      1  /* the draw was made by the fp64 path: the fp32 draw could not certify its token */
 #define SPECV_FLAG_ZW_ZERO   2  /* residual mass was zero after rounding; drew from p_n instead */
 #define SPECV_FLAG_BAD_DRAFT 4  /* an evaluated draft id was outside [0, V) and was rejected */
