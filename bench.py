@@ -38,6 +38,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import dataclasses
+import functools
 import hashlib
 import json
 import os
@@ -331,6 +332,104 @@ def ngram_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def ngram_map_bench(args):
+    """The n-gram map on the n-gram workload's histories: one table per history,
+    built once, then one update per step that adds the tokens a step appends to
+    every history (K + 1: every draft accepted, plus the bonus token) and
+    proposes.  The scan (spec_ngram_propose) is timed on the same lengths."""
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verify_spec_amd as sv
+    import workloads
+    lib = sv.load()
+    B, L, vocab, n_min, n_max, hits, K = 1024, 16384, 32000, 1, 4, 1, 5
+    add = K + 1
+    cap = 1 << (2 * (n_max - n_min + 1) * L - 1).bit_length()
+    log(f"generating {B} histories of up to {L} tokens; tables of {cap} slots")
+    hist, lens = workloads.make_histories(B, L, vocab, workers=workloads.default_workers())
+    nsteps = args.warmup + args.steps
+    start = lens - add * nsteps
+    if start.min() < 1:
+        print("--warmup + --steps too large for these histories", file=sys.stderr)
+        sys.exit(2)
+    steps_len = np.stack([start + add * i for i in range(nsteps + 1)]).astype(np.int32)  # [step][B]
+    h = torch.from_numpy(hist).cuda()
+    lens_dev = torch.from_numpy(steps_len).cuda()
+    zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
+    nbytes = sv.ngram_map_bytes(B, cap)
+    tables = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    spare = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    draft = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    count = torch.empty(B, dtype=torch.int32, device="cuda")
+    status = torch.empty(B, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    P = lambda t: t.data_ptr()
+    fn = lib.spec_ngram_map_update
+
+    def upd(tab, old_ptr, new_ptr):
+        return functools.partial(fn, P(tab), cap, P(h), old_ptr, new_ptr, B, L, n_min, n_max, hits, K, P(draft),
+                                 P(count), P(status), st)
+    row = lambda i: P(lens_dev) + 4 * B * i
+    build_spare = upd(spare, P(zeros), row(0))
+    ramp_steps, _, _ = warm_up(lambda: build_spare(), 1, args.ramp_seconds)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    assert upd(tables, P(zeros), row(0))() == 0
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+    calls = [upd(tables, row(i), row(i + 1)) for i in range(nsteps)]
+    for c in calls[:args.warmup]:
+        c()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for c in calls[args.warmup:]:
+        c()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    map_draft, map_count, map_status = draft.cpu().numpy(), count.cpu().numpy(), status.cpu().numpy()
+    # the scan on the final lengths, the same number of calls
+    final = lens_dev[nsteps]
+    sd = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    sc = torch.empty(B, dtype=torch.int32, device="cuda")
+    scan = functools.partial(lib.spec_ngram_propose, P(h), P(final), B, L, n_min, n_max, hits, K, P(sd), P(sc), st)
+    for _ in range(args.warmup):
+        scan()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        scan()
+    torch.cuda.synchronize()
+    scan_s = (time.perf_counter() - t0) / args.steps
+    mism = int(np.sum(np.any(map_draft != sd.cpu().numpy(), axis=1) | (map_count != sc.cpu().numpy())))
+    line = {"metric": "proposals/s, n-gram map update + lookup", "value": B / step_s, "unit": "proposals/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ramp_steps": ramp_steps,
+            "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "int32", "data": "synthetic",
+            "config": {"workload": f"ngram map: {B} histories, lengths uniform in [{L // 2}, {L}] less "
+                                   f"{add * nsteps} tokens at the build, {add} tokens added per history per "
+                                   f"step; vocab {vocab}, n = {n_min}..{n_max}, min hits {hits}, K = {K}",
+                       "B": B, "L_max": L, "capacity": cap, "table_bytes": nbytes},
+            "build_ms": build_s * 1e3, "scan_ms_per_step_same_lengths": scan_s * 1e3,
+            "map_vs_scan_mismatches": mism, "tables_full": int(np.count_nonzero(map_status)),
+            "proposal_rate": float(np.mean(map_count > 0)), "mean_draft": float(np.mean(map_count)),
+            "roofline": None, "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        from oracle import ngram
+        fl = steps_len[nsteps]
+        done, bad, t0 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds or done == 0:
+            b = done % B
+            d, c = ngram.propose_sequence(hist[b, : fl[b]], n_min, n_max, hits, K)
+            bad += int(c != map_count[b] or np.any(d != map_draft[b]))
+            done += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": done / dt, "unit": "proposals/s", "cores": 1, "kind": "oracle",
+                                "sample": f"{done} histories at the final lengths, numpy scan, one thread",
+                                "seconds": round(dt, 2), "sample_mismatches_vs_map": bad}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,6 +448,9 @@ def main():
                     help="greedy token-tree verification: 128 trees of 32 nodes, V=128256 bf16")
     ap.add_argument("--ngram", action="store_true",
                     help="prompt-lookup proposer: 1024 histories of up to 16384 tokens, n = 1..4, K = 5")
+    ap.add_argument("--ngram-map", action="store_true",
+                    help="n-gram map: the --ngram histories in hash tables, built once, then updated with 6 "
+                         "tokens per history per step")
     ap.add_argument("--full", action="store_true",
                     help="ask for every row's log Z, which sweeps every row at once instead of in rounds")
     ap.add_argument("--ragged", action="store_true",
@@ -372,6 +474,9 @@ def main():
         return
     if args.ngram:
         ngram_bench(args)
+        return
+    if args.ngram_map:
+        ngram_map_bench(args)
         return
     if args.copy_calibration > 0:
         src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")

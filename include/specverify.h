@@ -286,6 +286,58 @@ int spec_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int3
 int spec_ngram_propose(const int32_t* history, const int32_t* lengths, int B, int L_max, int n_min, int n_max,
                        int min_hits, int K, int32_t* out_draft, int32_t* out_count, void* stream);
 
+/*
+ * The n-gram map: spec_ngram_propose's proposals kept up to date in a hash
+ * table per sequence instead of rescanning the history on every call ([D]
+ * "Спекулятивное декодирование на n-граммах": the map variants key a hash
+ * table by the current n-gram and keep what followed it, for a lookup in
+ * place of the linear scan).  A table holds, for every n-gram of the sizes in
+ * use that a token follows, its count and its latest end; a call adds the
+ * n-grams whose following token is new and looks up the current suffix, so
+ * its cost follows the tokens added, not the history's length.
+ *
+ * spec_ngram_map_bytes - device bytes of B tables of `capacity` slots each
+ * (16 bytes a slot, plus 16 per table); 0 unless 1 <= B and capacity is a
+ * power of two in [SPECV_NGRAM_MAP_MIN_SLOTS, SPECV_NGRAM_MAP_MAX_SLOTS].  A
+ * table stays correct while it holds at most about half as many distinct
+ * n-grams as slots (n_max - n_min + 1 per token of history, at most).
+ */
+#define SPECV_NGRAM_MAP_MIN_SLOTS 64
+#define SPECV_NGRAM_MAP_MAX_SLOTS (1 << 28)
+#define SPECV_NGRAM_MAP_FULL      1   /* out_status: an insert found no free slot; the table is too small */
+size_t spec_ngram_map_bytes(int B, int capacity);
+
+/*
+ * spec_ngram_map_update - add each sequence's new tokens to its table and
+ * propose drafts from it.  For sequence b with previous length len_old[b] and
+ * length now len_new[b] (both clamped to [0, L_max], len_old to at most
+ * len_new): when len_old[b] is 0 its table is cleared and built from the
+ * whole history; otherwise the n-grams of sizes n_min..n_max ending at
+ * positions len_old[b] .. len_new[b] - 1 (those whose following token arrived
+ * since the previous call) are added.  Then the draft is what
+ * spec_ngram_propose returns for the history h[0..len_new[b]) with the same
+ * n_min, n_max, min_hits and K, unless two different n-grams of one history
+ * share a 64-bit key (probability about N^2 / 2^65 for N n-grams).
+ *   tables    spec_ngram_map_bytes(B, capacity) bytes of device memory, 16-byte
+ *             aligned, owned by the caller and kept between calls; its
+ *             contents are valid only for the same capacity, n_min and n_max,
+ *             and only when len_old[b] is the len_new[b] of the previous call
+ *             (or 0)
+ *   history, L_max, n_min, n_max, min_hits, K, out_draft, out_count: as for
+ *             spec_ngram_propose
+ *   len_old, len_new  [B] int32 (device)
+ *   out_status [B] int32 or NULL: 0, or SPECV_NGRAM_MAP_FULL when the table
+ *             has overflowed (since it was last built): then no draft is
+ *             proposed (count 0) until a call with len_old[b] == 0 rebuilds it
+ * Returns SPECV_OK, SPECV_E_NULL, SPECV_E_SHAPE (a size out of range, or
+ * spec_ngram_map_bytes(B, capacity) == 0), SPECV_E_ALIGN (tables) or
+ * SPECV_E_HIP; needs no workspace; nothing synchronises.  Calls on one table
+ * must not overlap.
+ */
+int spec_ngram_map_update(void* tables, int capacity, const int32_t* history, const int32_t* len_old,
+                          const int32_t* len_new, int B, int L_max, int n_min, int n_max, int min_hits, int K,
+                          int32_t* out_draft, int32_t* out_count, int32_t* out_status, void* stream);
+
 /* Device-side input validation, a debugging aid.  While it is on, every
  * spec_verify* call (spec_verify, _ex, _noalloc, _ragged, _ragged_ex) first
  * runs one more pass over the inputs it uses and adds what it finds to

@@ -33,6 +33,7 @@ EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_noalloc", "
            "spec_verify_sweep_timed",
            "spec_verify_ragged",
            "spec_verify_ragged_ex", "spec_verify_tree_workspace_size", "spec_verify_tree_greedy", "spec_tree_mask", "spec_ngram_propose",
+           "spec_ngram_map_bytes", "spec_ngram_map_update",
            "spec_debug_enable", "spec_debug_counters", "spec_debug_reset",
            "spec_verify_strerror", "spec_verify_version")
 
@@ -82,6 +83,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_tree_mask.restype = i32
     lib.spec_ngram_propose.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.spec_ngram_propose.restype = i32
+    lib.spec_ngram_map_bytes.argtypes = [i32, i32]
+    lib.spec_ngram_map_bytes.restype = sz
+    lib.spec_ngram_map_update.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.spec_ngram_map_update.restype = i32
     lib.spec_debug_enable.argtypes = [i32]
     lib.spec_debug_enable.restype = i32
     lib.spec_debug_counters.argtypes = [vp, i32]
@@ -406,3 +411,38 @@ def ngram_propose(history, lengths, n_min: int, n_max: int, min_hits: int, K: in
     if rc != 0:
         raise SpecVerifyError(rc, strerror(rc))
     return draft, count
+
+
+NGRAM_MAP_FULL = 1  # SPECV_NGRAM_MAP_FULL
+
+
+def ngram_map_bytes(B: int, capacity: int) -> int:
+    """Device bytes of B n-gram map tables of `capacity` slots (0 if invalid)."""
+    return int(load().spec_ngram_map_bytes(B, capacity))
+
+
+def ngram_map_update(tables, capacity: int, history, len_old, len_new, n_min: int, n_max: int, min_hits: int,
+                     K: int):
+    """spec_ngram_map_update on device tensors: tables (uint8, ngram_map_bytes
+    bytes, kept between calls), history [B, L_max] int32, len_old and len_new
+    [B] int32.  Returns (draft [B, K], count [B], status [B]) int32 device
+    tensors; nothing synchronises."""
+    import torch
+    dev = history.device
+    if dev.type != "cuda" or history.dtype != torch.int32 or history.dim() != 2 or not history.is_contiguous():
+        raise ValueError("history must be a contiguous int32 [B, L_max] device tensor")
+    B, L = history.shape
+    for name, t in (("len_old", len_old), ("len_new", len_new)):
+        if t.device != dev or t.dtype != torch.int32 or tuple(t.shape) != (B,):
+            raise ValueError(f"{name} must be an int32 [B] tensor on the history's device")
+    if tables.device != dev or tables.numel() * tables.element_size() < ngram_map_bytes(B, capacity):
+        raise ValueError("tables must be a device tensor of ngram_map_bytes(B, capacity) bytes")
+    draft = torch.empty((B, K), dtype=torch.int32, device=dev)
+    count = torch.empty((B,), dtype=torch.int32, device=dev)
+    status = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    rc = int(load().spec_ngram_map_update(_ptr(tables), capacity, _ptr(history), _ptr(len_old), _ptr(len_new), B, L,
+                                          n_min, n_max, min_hits, K, _ptr(draft), _ptr(count), _ptr(status), st))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_ngram_map_update")
+    return draft, count, status

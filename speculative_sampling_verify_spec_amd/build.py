@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
 SOURCES = ["api.cpp", "k_sweep.hip", "k_rounds.hip", "k_verify.hip", "k_exact.hip", "k_short.hip", "k_greedy.hip", "k_stats.hip",
-           "k_tree.hip", "k_ngram.hip", "k_validate.hip"]
+           "k_tree.hip", "k_ngram.hip", "k_ngram_map.hip", "k_validate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -547,6 +547,27 @@ int spec_ngram_propose(const int32_t* history, const int32_t* lengths, int B, in
   return SPECV_OK;
 }
 
+size_t spec_ngram_map_bytes(int B, int capacity) {
+  if (B < 1 || capacity < SPECV_NGRAM_MAP_MIN_SLOTS || capacity > SPECV_NGRAM_MAP_MAX_SLOTS ||
+      (capacity & (capacity - 1)) != 0)
+    return 0;
+  return static_cast<size_t>(B) * (16 + 16 * static_cast<size_t>(capacity));
+}
+
+int spec_ngram_map_update(void* tables, int capacity, const int32_t* history, const int32_t* len_old,
+                          const int32_t* len_new, int B, int L_max, int n_min, int n_max, int min_hits, int K,
+                          int32_t* out_draft, int32_t* out_count, int32_t* out_status, void* stream) {
+  if (!tables || !history || !len_old || !len_new || !out_draft || !out_count) return SPECV_E_NULL;
+  if (spec_ngram_map_bytes(B, capacity) == 0 || L_max < 1 || n_min < 1 || n_max < n_min ||
+      n_max > SPECV_MAX_NGRAM || min_hits < 1 || K < 1 || K > SPECV_MAX_K)
+    return SPECV_E_SHAPE;
+  if (reinterpret_cast<uintptr_t>(tables) % 16) return SPECV_E_ALIGN;
+  if (sv::launch_ngram_map(tables, capacity, history, len_old, len_new, B, L_max, n_min, n_max, min_hits, K,
+                           out_draft, out_count, out_status, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SPECV_E_HIP;
+  return SPECV_OK;
+}
+
 int spec_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int32_t* out_depth, void* stream) {
   if (!parents || (!out_mask && !out_depth)) return SPECV_E_NULL;
   if (B < 1 || N < 1 || N > SPECV_MAX_TREE || static_cast<long>(B) * N * N >= (1L << 40)) return SPECV_E_SHAPE;

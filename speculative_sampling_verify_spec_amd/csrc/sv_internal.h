@@ -199,6 +199,9 @@ unsigned long long* debug_counters_ptr();  // the current device's counters, or 
 hipError_t launch_tree_scan(const Params& p, hipStream_t s);
 hipError_t launch_ngram(const int32_t* hist, const int32_t* lengths, int B, int Lmax, int n_min, int n_max,
                         int min_hits, int K, int32_t* out_draft, int32_t* out_count, hipStream_t s);
+hipError_t launch_ngram_map(void* tables, int capacity, const int32_t* hist, const int32_t* len_old,
+                            const int32_t* len_new, int B, int Lmax, int n_min, int n_max, int min_hits, int K,
+                            int32_t* out_draft, int32_t* out_count, int32_t* out_status, hipStream_t s);
 hipError_t launch_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int32_t* out_depth,
                             hipStream_t s);
 

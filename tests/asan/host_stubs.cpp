@@ -19,6 +19,10 @@ hipError_t launch_ngram(const int32_t*, const int32_t*, int, int, int, int, int,
                         hipStream_t) {
   return hipErrorInvalidValue;
 }
+hipError_t launch_ngram_map(void*, int, const int32_t*, const int32_t*, const int32_t*, int, int, int, int, int,
+                            int, int32_t*, int32_t*, int32_t*, hipStream_t) {
+  return hipErrorInvalidValue;
+}
 hipError_t launch_tree_mask(const int32_t*, int, int, uint8_t*, int32_t*, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_validate(const Params&, int, bool, unsigned long long*, hipStream_t) { return hipErrorInvalidValue; }
 bool debug_enabled_flag(int* set_to) {

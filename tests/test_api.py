@@ -182,6 +182,23 @@ def test_ngram_entry_point_checks_arguments(lib):
         assert call(**bad) == -2, bad
 
 
+def test_ngram_map_entry_points_check_arguments(lib):
+    assert lib.spec_ngram_map_bytes(4, 1024) == 4 * (16 + 16 * 1024)
+    for B, cap in [(0, 1024), (4, 32), (4, 1000), (4, 1 << 29), (-1, 64)]:
+        assert lib.spec_ngram_map_bytes(B, cap) == 0, (B, cap)
+    T, H, LO, LN, D, C, S = (0x100000 * i for i in range(1, 8))
+    call = lambda **k: lib.spec_ngram_map_update(k.get("t", T), k.get("cap", 1024), k.get("h", H), k.get("lo", LO),
+                                                  k.get("ln", LN), k.get("B", 4), k.get("L", 100),
+                                                  k.get("nmin", 1), k.get("nmax", 4), k.get("hits", 1),
+                                                  k.get("K", 5), k.get("d", D), k.get("c", C), k.get("s", S), None)
+    for name in ("t", "h", "lo", "ln", "d", "c"):
+        assert call(**{name: None}) == -1, name
+    for bad in [dict(B=0), dict(L=0), dict(nmin=0), dict(nmin=3, nmax=2), dict(nmax=17), dict(hits=0),
+                dict(K=0), dict(K=33), dict(cap=1000), dict(cap=32)]:
+        assert call(**bad) == -2, bad
+    assert call(t=T + 8) == -6
+
+
 def test_noalloc_entry_point_checks(lib):
     """spec_verify_noalloc runs spec_verify's host-side checks, and rejects a
     shape whose workspace exceeds its static scratch before any HIP call."""
