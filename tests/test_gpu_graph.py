@@ -21,6 +21,7 @@ CASES = {
     "small-16": lambda: workloads.make_batch(1, seqs=range(16)),
     "headline-16-split": lambda: workloads.make_batch(2, seqs=range(16), workers=workloads.default_workers()),
     "small-160": lambda: workloads.make_batch(1, seqs=range(160), workers=workloads.default_workers()),
+    "short-rows-48": lambda: workloads.make_batch(0, seqs=range(48)),  # one launch (k_short)
 }
 
 
