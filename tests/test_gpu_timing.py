@@ -80,3 +80,30 @@ def test_each_sweep_launch_is_timed(gpu_lib):
         assert rc == 0 and ns == 3
     finally:
         ev.close()
+
+
+def test_short_rows_one_launch_is_timed(gpu_lib):
+    """Rows of at most 2048 tokens take one launch for the whole step: the
+    timed entry point reports one launch, times it with the first pair, and
+    gives spec_verify_ex's outputs."""
+    sv = gpu_lib
+    b = workloads.make_batch(0, seqs=range(16))
+    lp, lq, x, ua, ur = workloads.to_device(b)
+    B, K, V, T = b.B, b.K, b.V, b.T
+    ws = torch.empty(sv.workspace_size(B, K, V, sv.SPECV_F32, T), dtype=torch.uint8, device="cuda")
+    rt = torch.full((B, K + 1), -7, dtype=torch.int32, device="cuda")
+    rn = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    rf = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    assert sv.spec_verify(lp, lq, x, ua, ur, T, rt, rn, ws, out_flags=rf, extended=True) == 0
+    ev = _Events(3)
+    try:
+        t, n, f = torch.empty_like(rt), torch.empty_like(rn), torch.empty_like(rf)
+        rc, ns = sv.spec_verify_sweep_timed(lp, lq, x, ua, ur, T, t, n, ws, ev.begin, ev.end, out_flags=f)
+        torch.cuda.synchronize()
+        assert rc == 0 and ns == 1, (rc, ns)
+        assert ev.ms(ev.begin[0], ev.end[0]) > 0
+        for got, ref in ((t, rt), (n, rn), (f, rf)):
+            np.testing.assert_array_equal(got.cpu().numpy(), ref.cpu().numpy())
+        assert np.all(f.cpu().numpy() & sv.FLAG_FP64)
+    finally:
+        ev.close()
