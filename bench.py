@@ -126,6 +126,25 @@ def counter_traffic(swept_bytes: int):
     return float(m_bytes.group(1))
 
 
+def acceptance_summary(n, kb, K: int) -> dict:
+    """Acceptance as the pages' monitoring advice asks for it ([D] "Мониторинг в
+    производстве": acceptance by position), from one call's counts: the share
+    of the sequences that tested position k (k < K_b, no rejection before k)
+    that accepted it; the overall rate beta over all tests; the tokens a round
+    emits (accepted + 1) as measured, and as the pages' formula predicts for
+    i.i.d. acceptance beta and K drafts ([B] "加速比公式：什么时候值得投机？":
+    E[N] = (1 - beta^(K+1)) / (1 - beta))."""
+    import numpy as np
+    n, kb = np.asarray(n), np.asarray(kb)
+    tested = np.array([int(np.sum((n >= k) & (kb > k))) for k in range(K)])
+    accepted = np.array([int(np.sum(n > k)) for k in range(K)])
+    beta = float(accepted.sum() / max(tested.sum(), 1))
+    pred = float(K + 1) if beta >= 1.0 else (1.0 - beta ** (K + 1)) / (1.0 - beta)
+    return {"per_position": [round(float(a / t), 4) if t else None for a, t in zip(accepted, tested)],
+            "tested": tested.tolist(), "beta": round(beta, 4),
+            "tokens_per_round": float(np.mean(n + 1)), "tokens_per_round_predicted_iid": round(pred, 4)}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -611,6 +630,7 @@ def main():
                            "needed": needed, "rows_needed": rows_needed, "all_rows": swept_all,
                            "rows_all": rows_all},
         "mean_accepted": float(np.mean(n_host)),
+        "acceptance": acceptance_summary(n_host, kb_host if args.ragged else np.full(B, K), K),
         "input_copies": ncopy,
         "fp64_draw_fraction": None if (greedy or args.ragged) else float(np.mean((flags.cpu().numpy() & sv.FLAG_FP64) != 0)),
         "roofline": None,

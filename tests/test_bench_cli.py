@@ -21,3 +21,17 @@ def test_negative_seqs_is_refused():
     r = run("--workload", "1", "--seqs", "-1")
     assert r.returncode == 2
     assert "--seqs" in r.stderr
+
+
+def test_acceptance_summary():
+    """Per-position acceptance from counts, and the pages' E[N] formula at the
+    measured rate (host arithmetic only)."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    a = bench.acceptance_summary(np.array([0, 1, 1]), np.array([1, 1, 2]), 2)
+    assert a["tested"] == [3, 1] and a["per_position"] == [0.6667, 0.0] and a["beta"] == 0.5
+    assert abs(a["tokens_per_round"] - 5 / 3) < 1e-12 and a["tokens_per_round_predicted_iid"] == 1.75
+    full = bench.acceptance_summary(np.array([3, 3]), np.array([3, 3]), 3)
+    assert full["beta"] == 1.0 and full["tokens_per_round_predicted_iid"] == 4.0
+    assert full["per_position"] == [1.0, 1.0, 1.0]
