@@ -287,6 +287,19 @@ int spec_ngram_propose(const int32_t* history, const int32_t* lengths, int B, in
                        int min_hits, int K, int32_t* out_draft, int32_t* out_count, void* stream);
 
 /*
+ * spec_rounds_min_bytes - the input size from which the verify calls read
+ * logit rows in rounds and skip the rows past each sequence's first
+ * rejection (and token trees the rows below a rejected node): checking
+ * stops there ([B] "多 Token 验证：左到右，遇错即停").  Smaller inputs take one
+ * sweep of every row, whose fewer launches cost less than the rows they would
+ * skip.  The default is 256 MiB of logit rows, or SPECV_ROUNDS_MIN_BYTES from
+ * the environment at the first use.  bytes >= 0 sets the threshold for the
+ * process and returns the previous one; a negative (or non-finite) value only
+ * returns it.  Both ways give the same outputs.
+ */
+double spec_rounds_min_bytes(double bytes);
+
+/*
  * The n-gram map: spec_ngram_propose's proposals kept up to date in a hash
  * table per sequence instead of rescanning the history on every call ([D]
  * "Спекулятивное декодирование на n-граммах": the map variants key a hash

@@ -33,7 +33,7 @@ EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_noalloc", "
            "spec_verify_sweep_timed",
            "spec_verify_ragged",
            "spec_verify_ragged_ex", "spec_verify_tree_workspace_size", "spec_verify_tree_greedy", "spec_tree_mask", "spec_ngram_propose",
-           "spec_ngram_map_bytes", "spec_ngram_map_update",
+           "spec_ngram_map_bytes", "spec_ngram_map_update", "spec_rounds_min_bytes",
            "spec_debug_enable", "spec_debug_counters", "spec_debug_reset",
            "spec_verify_strerror", "spec_verify_version")
 
@@ -83,6 +83,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_tree_mask.restype = i32
     lib.spec_ngram_propose.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.spec_ngram_propose.restype = i32
+    lib.spec_rounds_min_bytes.argtypes = [ctypes.c_double]
+    lib.spec_rounds_min_bytes.restype = ctypes.c_double
     lib.spec_ngram_map_bytes.argtypes = [i32, i32]
     lib.spec_ngram_map_bytes.restype = sz
     lib.spec_ngram_map_update.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -446,3 +448,9 @@ def ngram_map_update(tables, capacity: int, history, len_old, len_new, n_min: in
     if rc != 0:
         raise SpecVerifyError(rc, "spec_ngram_map_update")
     return draft, count, status
+
+
+def rounds_min_bytes(bytes_: Optional[float] = None) -> float:
+    """The input size from which verify calls read rows in rounds (early
+    exit); sets it when bytes_ is given.  Returns the previous value."""
+    return float(load().spec_rounds_min_bytes(-1.0 if bytes_ is None else float(bytes_)))

@@ -2,6 +2,7 @@
 // launch sequence of one verify step.  Nothing here allocates, synchronises
 // or keeps state between calls.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -68,6 +69,10 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy, bool t
   L.kbs = off;
   off = align_up(off + static_cast<size_t>(B) * sizeof(int32_t));
   if (greedy) {
+    if (tree) {  // token trees read in rounds: per node, whether the round reads its row
+      L.tneed = off;
+      off = align_up(off + static_cast<size_t>(B) * (K + 1));
+    }
     L.total = off;
     return L;
   }
@@ -145,20 +150,23 @@ int verify_split(int B, int V, int dtype, bool vec) {
 }
 
 // Bytes of logit rows from which the sweep runs in rounds: kRoundsMinBytes,
-// or SPECV_ROUNDS_MIN_BYTES from the environment (read once per process).
-double rounds_min_bytes() {
-  static std::once_flag once;
-  static double v = kRoundsMinBytes;
-  std::call_once(once, [] {
+// or SPECV_ROUNDS_MIN_BYTES from the environment (read at the first use), or
+// what spec_rounds_min_bytes set.
+std::atomic<double>& rounds_threshold() {
+  static std::atomic<double> v{[] {
+    double t = kRoundsMinBytes;
     const char* e = std::getenv("SPECV_ROUNDS_MIN_BYTES");
     if (e && *e) {
       char* end = nullptr;
       const double d = std::strtod(e, &end);
-      if (end != e && d >= 0.0) v = d;
+      if (end != e && d >= 0.0) t = d;
     }
-  });
+    return t;
+  }()};
   return v;
 }
+
+double rounds_min_bytes() { return rounds_threshold().load(std::memory_order_relaxed); }
 
 // Largest batch that takes the one-launch path for short rows (k_short):
 // kShortSeqsPerCU sequences per CU, or SPECV_SHORT_MAX_SEQS from the
@@ -530,7 +538,26 @@ int spec_verify_tree_greedy(const void* logits, const int32_t* tree_tokens, cons
   P.cr = L.cr;
   P.sweep_large = L.sweep_large;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (launch_sweep_argmax(P, dtype, st, nullptr, nullptr) != hipSuccess) return SPECV_E_HIP;
+  // rounds by depth on large inputs, as for draft positions: the roots, then
+  // depths 1-2, then the rest, each after k_tree_round has marked the rows
+  // the round needs
+  const bool rounds = N > 1 && static_cast<double>(B) * N * V * eb >= rounds_min_bytes();
+  if (!rounds) {
+    if (launch_sweep_argmax(P, dtype, st, nullptr, nullptr) != hipSuccess) return SPECV_E_HIP;
+  } else {
+    P.tneed = reinterpret_cast<uint8_t*>(static_cast<char*>(workspace) + L.tneed);
+    P.grid3 = 1;
+    P.lv0 = 0;
+    P.lv1 = 1;
+    if (launch_sweep_argmax(P, dtype, st, nullptr, nullptr) != hipSuccess) return SPECV_E_HIP;
+    P.lv0 = 1;
+    P.lv1 = N;
+    const int d[3] = {1, 3, SPECV_MAX_TREE};  // depth bounds of the later rounds
+    for (int r = 0; r < 2 && d[r] < N; ++r) {  // a tree of N nodes has depths below N
+      if (launch_tree_round(P, d[r], d[r + 1], st) != hipSuccess) return SPECV_E_HIP;
+      if (launch_sweep_argmax_tree(P, dtype, st) != hipSuccess) return SPECV_E_HIP;
+    }
+  }
   if (launch_tree_scan(P, st) != hipSuccess) return SPECV_E_HIP;
   return SPECV_OK;
 }
@@ -574,6 +601,11 @@ int spec_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int3
   if (sv::launch_tree_mask(parents, B, N, out_mask, out_depth, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SPECV_E_HIP;
   return SPECV_OK;
+}
+
+double spec_rounds_min_bytes(double bytes) {
+  std::atomic<double>& t = sv::rounds_threshold();
+  return bytes >= 0.0 && std::isfinite(bytes) ? t.exchange(bytes) : t.load();
 }
 
 int spec_debug_enable(int on) { return sv::debug_enabled_flag(&on) ? 1 : 0; }

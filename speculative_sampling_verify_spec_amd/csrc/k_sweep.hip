@@ -219,7 +219,9 @@ __global__ __launch_bounds__(kBlock) void k_sweep_lse(Params p) {
   if (G3 && p.lv0 == 0 && first_block()) reset_state(p);
 }
 
-template <int DT, bool VEC, bool LARGE, bool G3>
+// TREE: a later round of token-tree rows (3-D grid, slots = nodes lv0..lv1-1):
+// a node's row is read when k_tree_round marked it.
+template <int DT, bool VEC, bool LARGE, bool G3, bool TREE = false>
 __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
   constexpr int N = kSweepElems<DT, VEC, true, LARGE>();
   constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
@@ -227,7 +229,9 @@ __global__ __launch_bounds__(kBlock) void k_sweep_argmax(Params p) {
   const uint32_t chunk = q.chunk, row = q.row;
   // target rows past a sequence's own draft count are not read, nor, in a
   // later round, those of a sequence whose drafts stopped matching
-  if constexpr (G3) {
+  if constexpr (TREE) {
+    if (!p.tneed[static_cast<long>(q.seq) * (p.K + 1) + q.level]) return;
+  } else if constexpr (G3) {
     if (q.level > sweep_kb(p, q.seq)) return;
   } else if (p.kb) {  // never true as launched; see sweep_pos
     const uint32_t s = row / (p.K + 1u), j = row - s * (p.K + 1u);
@@ -312,6 +316,15 @@ hipError_t launch_argmax(const Params& p, hipStream_t st, hipEvent_t e0, hipEven
   return launch_grid(k_sweep_argmax<DT, true, false, G3>, G3, slots, p, st, e0, e1);
 }
 
+template <int DT>
+hipError_t launch_argmax_tree(const Params& p, hipStream_t st) {
+  const unsigned slots = static_cast<unsigned>(p.lv1 - p.lv0);
+  if (!p.vec) return launch_grid(k_sweep_argmax<DT, false, false, true, true>, true, slots, p, st, nullptr, nullptr);
+  if (p.sweep_large)
+    return launch_grid(k_sweep_argmax<DT, true, true, true, true>, true, slots, p, st, nullptr, nullptr);
+  return launch_grid(k_sweep_argmax<DT, true, false, true, true>, true, slots, p, st, nullptr, nullptr);
+}
+
 hipError_t launch_sweep_lse(const Params& p, int dtype, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const bool g3 = p.grid3 != 0;
   if (dtype == 1) return g3 ? launch_lse<1, true>(p, st, e0, e1) : launch_lse<1, false>(p, st, e0, e1);
@@ -322,6 +335,10 @@ hipError_t launch_sweep_argmax(const Params& p, int dtype, hipStream_t st, hipEv
   const bool g3 = p.grid3 != 0;
   if (dtype == 1) return g3 ? launch_argmax<1, true>(p, st, e0, e1) : launch_argmax<1, false>(p, st, e0, e1);
   return g3 ? launch_argmax<0, true>(p, st, e0, e1) : launch_argmax<0, false>(p, st, e0, e1);
+}
+
+hipError_t launch_sweep_argmax_tree(const Params& p, int dtype, hipStream_t st) {
+  return dtype == 1 ? launch_argmax_tree<1>(p, st) : launch_argmax_tree<0>(p, st);
 }
 
 }  // namespace sv

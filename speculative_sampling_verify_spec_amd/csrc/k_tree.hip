@@ -93,6 +93,50 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree_scan(Params p) {
   }
 }
 
+// Between two rounds of a tree's rows (token trees read in rounds by depth):
+// rows of depth < d0 have been swept where needed, which decides the edge
+// test of every node of depth <= d0.  The nodes the next round reads are
+// those of depth in [d0, d1) whose ancestors of depth <= d0 (itself included
+// at depth d0) are all accepted: a row is needed only once its node is
+// accepted, and a round reads its deeper rows ahead of their own tests.
+// Rows of shallower nodes that were not swept hold stale arg-maxes; they can
+// only decide the tests of children whose parent is not accepted, which
+// acceptance masks (the same holds in k_tree_scan after the last round).
+__global__ __launch_bounds__(kTreeBlock) void k_tree_round(Params p, int d0, int d1) {
+  const long s = blockIdx.x;
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int N = p.K + 1, np = p.nch1 * kWaves;
+  __shared__ int sA[kWave];
+  uint64_t set;
+  bool valid;
+  int depth;
+  ancestor_sets(p.parents + s * N, N, set, valid, depth);  // in every wave: which rows are shallow
+  const uint64_t shallow = static_cast<uint64_t>(__ballot(lane < N && depth < d0));
+  for (int i = w; i < N; i += kTreeWaves) {
+    if (!((shallow >> i) & 1ull)) continue;  // uniform over the wave
+    const float2* pr = p.part + (s * N + i) * np;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int j = lane; j < np; j += kWave) argmax_merge(bv, bi, pr[j].x, __float_as_int(pr[j].y));
+    wave_argmax(bv, bi);
+    if (lane == 0) sA[i] = bi;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  const int v = lane;
+  const int tok = v < N ? p.x[s * N + v] : 0;
+  const int pv = v < N ? p.parents[s * N + v] : -1;
+  const int pa = (v > 0 && v < N && valid) ? pv : 0;  // a parent in [0, v), or 0 (read and unused)
+  const bool tested = v < N && depth <= d0;
+  const bool edge_ok = v == 0 || (tested && valid && tok == sA[pa]);
+  // nodes deeper than d0 lie in no set of a node of depth <= d0
+  const uint64_t ok = static_cast<uint64_t>(__ballot(edge_ok || !tested));
+  const uint64_t acc = static_cast<uint64_t>(__ballot(tested && (set & ~ok) == 0));
+  const uint64_t upto = static_cast<uint64_t>(__ballot(tested));
+  const bool need = v < N && depth >= d0 && depth < d1 && (set & upto & ~acc) == 0;
+  if (v < N) p.tneed[s * N + v] = need ? 1 : 0;
+}
+
 __global__ __launch_bounds__(kWave) void k_tree_mask(const int32_t* parents, int N, uint8_t* out_mask,
                                                      int32_t* out_depth) {
   const long s = blockIdx.x;
@@ -114,6 +158,11 @@ __global__ __launch_bounds__(kWave) void k_tree_mask(const int32_t* parents, int
 
 hipError_t launch_tree_scan(const Params& p, hipStream_t st) {
   hipLaunchKernelGGL(k_tree_scan, dim3(static_cast<unsigned>(p.nseq)), dim3(kTreeBlock), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_round(const Params& p, int d0, int d1, hipStream_t st) {
+  hipLaunchKernelGGL(k_tree_round, dim3(static_cast<unsigned>(p.nseq)), dim3(kTreeBlock), 0, st, p, d0, d1);
   return hipGetLastError();
 }
 

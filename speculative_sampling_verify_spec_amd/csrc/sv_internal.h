@@ -48,6 +48,9 @@ constexpr long kSweepLargeMinGroups = 6144;
 constexpr int kMaxRounds = 3;
 constexpr int kMaxRoundLevels = 2;  // levels of a round that another round follows
 __host__ __device__ constexpr int round_begin(int r) { return r == 0 ? 0 : (r == 1 ? 1 : 3); }
+// Token trees read their rows in the same rounds, by depth: the root, then
+// depths 1-2, then the rest (a node's row is needed only once the node is
+// accepted, and acceptance descends from the root).
 constexpr double kRoundsMinBytes = 256.0 * (1 << 20);
 
 // The fast draw (k_verify) streams a sequence's decisive row(s) in wave
@@ -156,6 +159,7 @@ struct Params {
   int lv0, lv1;              // grid3: the levels the launch covers (target rows lv0..lv1-1, and the
                              // draft rows among them); lv0 > 0: skip the rows past kbs[s]
   int32_t* kbs;              // [B] rounds: the last level still to sweep per sequence (k_round_accept)
+  uint8_t* tneed;            // token trees in rounds: [B][N] 1 where the round sweeps the node's row (k_tree_round)
   int vwaves;                // k_verify's waves per workgroup when unsplit: kVerifyWaves or kVerifyWavesSmall
   int vpre;                  // k_verify, rounds: the last round's first level (sequences with kbs below it
                              // were decided earlier); 0 after a one-sweep call
@@ -175,7 +179,7 @@ struct Params {
 
 // Workspace layout (byte offsets), shared by spec_verify_workspace_size and the launcher.
 struct Layout {
-  size_t part, kbs, xsum, queue, qcount, segm, spq, vcount, total;
+  size_t part, kbs, tneed, xsum, queue, qcount, segm, spq, vcount, total;
   int nch1, ch1, cq, cr, R3, ch3;
   int sweep_large;  // the sweep's large shape (see kSweepElems)
 };
@@ -197,6 +201,8 @@ hipError_t launch_validate(const Params& p, int dtype, bool greedy, unsigned lon
 bool debug_enabled_flag(int* set_to);
 unsigned long long* debug_counters_ptr();  // the current device's counters, or null
 hipError_t launch_tree_scan(const Params& p, hipStream_t s);
+hipError_t launch_tree_round(const Params& p, int d0, int d1, hipStream_t s);
+hipError_t launch_sweep_argmax_tree(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_ngram(const int32_t* hist, const int32_t* lengths, int B, int Lmax, int n_min, int n_max,
                         int min_hits, int K, int32_t* out_draft, int32_t* out_count, hipStream_t s);
 hipError_t launch_ngram_map(void* tables, int capacity, const int32_t* hist, const int32_t* len_old,

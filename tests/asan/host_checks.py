@@ -22,6 +22,7 @@ sigs = {
     "spec_tree_mask": ([vp, i32, i32, vp, vp, vp], i32),
     "spec_ngram_propose": ([vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp], i32),
     "spec_ngram_map_bytes": ([i32, i32], sz),
+    "spec_rounds_min_bytes": ([ctypes.c_double], ctypes.c_double),
     "spec_ngram_map_update": ([vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp], i32),
     "spec_verify_strerror": ([i32], ctypes.c_char_p),
     "spec_verify_version": ([], ctypes.c_char_p),
@@ -91,6 +92,9 @@ assert lib.spec_tree_mask(PA, 4, 16, OTT, OP, None) == -7
 assert lib.spec_ngram_propose(L, TT, 4, 100, 3, 2, 1, 5, OTT, OP, None) == -2
 assert lib.spec_ngram_propose(L, TT, 4, 100, 1, 4, 1, 5, OTT, OP, None) == -7
 assert lib.spec_ngram_map_bytes(4, 1024) == 4 * (16 + 16 * 1024) and lib.spec_ngram_map_bytes(4, 1000) == 0
+old = lib.spec_rounds_min_bytes(-1.0)
+assert lib.spec_rounds_min_bytes(12345.0) == old and lib.spec_rounds_min_bytes(float("nan")) == 12345.0
+assert lib.spec_rounds_min_bytes(old) == 12345.0
 assert lib.spec_ngram_map_update(WS, 1024, L, TT, PA, 4, 100, 3, 2, 1, 5, OTT, OP, None, None) == -2
 assert lib.spec_ngram_map_update(WS + 8, 1024, L, TT, PA, 4, 100, 1, 4, 1, 5, OTT, OP, None, None) == -6
 assert lib.spec_ngram_map_update(WS, 1024, L, TT, PA, 4, 100, 1, 4, 1, 5, OTT, OP, None, None) == -7

@@ -15,6 +15,8 @@ hipError_t launch_greedy_scan(const Params&, hipStream_t) { return hipErrorInval
 hipError_t launch_round_accept(const Params&, int, bool, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_position_stats(const Params&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_tree_scan(const Params&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_tree_round(const Params&, int, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_sweep_argmax_tree(const Params&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_ngram(const int32_t*, const int32_t*, int, int, int, int, int, int, int32_t*, int32_t*,
                         hipStream_t) {
   return hipErrorInvalidValue;

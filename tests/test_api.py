@@ -199,6 +199,16 @@ def test_ngram_map_entry_points_check_arguments(lib):
     assert call(t=T + 8) == -6
 
 
+def test_rounds_threshold_knob(lib):
+    old = lib.spec_rounds_min_bytes(-1.0)
+    try:
+        assert lib.spec_rounds_min_bytes(1e9) == old
+        assert lib.spec_rounds_min_bytes(-5.0) == 1e9 and lib.spec_rounds_min_bytes(float("inf")) == 1e9
+    finally:
+        lib.spec_rounds_min_bytes(old)
+    assert lib.spec_rounds_min_bytes(-1.0) == old
+
+
 def test_noalloc_entry_point_checks(lib):
     """spec_verify_noalloc runs spec_verify's host-side checks, and rejects a
     shape whose workspace exceeds its static scratch before any HIP call."""

@@ -35,3 +35,19 @@ def test_acceptance_summary():
     full = bench.acceptance_summary(np.array([3, 3]), np.array([3, 3]), 3)
     assert full["beta"] == 1.0 and full["tokens_per_round_predicted_iid"] == 4.0
     assert full["per_position"] == [1.0, 1.0, 1.0]
+
+
+def test_tree_rows_read():
+    """Rows a chain of five nodes needs in rounds by depth: the root, depths
+    1-2 under an accepted depth-1 node, deeper nodes under an accepted depth-3
+    node."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    lg = np.zeros((1, 5, 4), np.float32)
+    lg[:, :, 0] = 1.0  # every row's arg-max is token 0
+    par = np.array([[-1, 0, 1, 2, 3]], np.int32)
+    assert bench.tree_rows_read(lg, np.array([[9, 0, 0, 1, 0]], np.int32), par, "fp32", True) == 3
+    assert bench.tree_rows_read(lg, np.array([[9, 0, 0, 0, 0]], np.int32), par, "fp32", True) == 5
+    assert bench.tree_rows_read(lg, np.array([[9, 2, 0, 0, 0]], np.int32), par, "fp32", True) == 1
+    assert bench.tree_rows_read(lg, np.array([[9, 2, 0, 0, 0]], np.int32), par, "fp32", False) == 5

@@ -43,6 +43,47 @@ def test_tree_verification_matches_oracle(gpu_lib, B, N, V, dt, pb):
     np.testing.assert_array_equal(path.cpu().numpy(), rp)
 
 
+def _run_tree(sv, tb):
+    import torch
+    tok, path, n = sv.verify_tree_greedy(_logits_dev(tb), _dev(tb.tokens), _dev(tb.parents))
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), path.cpu().numpy(), n.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,N,V,dt,pb,all_match", [(8, 2, 3000, "bf16", 0.5, False), (8, 3, 3000, "fp32", 0.0, False),
+                                                   (8, 4, 3000, "bf16", 0.0, True), (16, 64, 4096, "bf16", 0.0, False),
+                                                   (16, 64, 4096, "fp32", 0.0, True), (32, 48, 2048, "bf16", 1.0, True),
+                                                   (24, 32, 5001, "fp32", 0.5, False)],
+                         ids=lambda x: str(x))
+def test_tree_rounds_and_full_sweep_agree(gpu_lib, B, N, V, dt, pb, all_match):
+    """Token trees read in rounds by depth (the roots, depths 1-2, the rest,
+    with k_tree_round marking the rows each round needs) and with every row
+    swept at once give the oracle's outputs.  Chains (p_branch 0), bushy
+    trees (p_branch 1), the round boundaries (N = 2, 3, 4) and trees whose
+    every token is its parent's arg-max (every row needed)."""
+    tb = workloads.make_tree_batch(B, N, V, dt, seed=3 * N + V, p_branch=pb, workers=workloads.default_workers())
+    if all_match:  # every node's token is its parent's first arg-max: every node is accepted
+        amax = np.argmax(workloads.storage_to_f64(tb.logits, dt), axis=2)
+        for b in range(B):
+            for v in range(1, N):
+                tb.tokens[b, v] = amax[b, tb.parents[b, v]]
+    say(f"[tree] rounds vs full: B={B} N={N} V={V} {dt} p_branch={pb} all_match={all_match}")
+    rt, rp, rn = tree.verify_tree_greedy(tb.logits, tb.tokens, tb.parents, tb.dtype)
+    old = gpu_lib.rounds_min_bytes(0.0)
+    try:
+        got_rounds = _run_tree(gpu_lib, tb)
+        gpu_lib.rounds_min_bytes(1e18)
+        got_full = _run_tree(gpu_lib, tb)
+    finally:
+        gpu_lib.rounds_min_bytes(old)
+    for got, name in ((got_rounds, "rounds"), (got_full, "full")):
+        np.testing.assert_array_equal(got[2], rn, err_msg=name)
+        np.testing.assert_array_equal(got[0], rt, err_msg=name)
+        np.testing.assert_array_equal(got[1], rp, err_msg=name)
+    if all_match:
+        assert np.all(rn == np.array([max(tree.tree_mask(tb.parents[b])[1]) for b in range(B)]))
+
+
 @pytest.mark.parametrize("N", [1, 2, 5, 33, 64])
 def test_tree_mask_matches_oracle(gpu_lib, N):
     import torch
