@@ -122,3 +122,43 @@ def test_long_histories_match_the_scan(gpu_lib):
     rd, rc = ngram.propose(hist, old, n_min, n_max, hits, K)
     np.testing.assert_array_equal(c, rc)
     np.testing.assert_array_equal(d, rd)
+
+
+N_RANDOM_MAP = int(__import__("os").environ.get("SPECV_RANDOM_MAP_CASES", "8"))
+
+
+@pytest.mark.parametrize("case", range(N_RANDOM_MAP))
+def test_random_map_schedules_match_oracle(gpu_lib, case):
+    """Random histories, sizes, hits, K and growth schedules (one to K + 1
+    tokens per step, some steps adding none, some sequences rebuilt midway
+    with previous length 0) against the oracle after every call."""
+    import torch
+    rng = np.random.default_rng(6000 + case)
+    B = int(rng.integers(1, 24))
+    L = int(rng.choice([40, 300, 2000, 5000]))
+    vocab = int(rng.choice([2, 7, 300, 32000]))
+    n_max = int(rng.integers(1, 17))
+    n_min = int(rng.integers(1, n_max + 1))
+    hits = int(rng.integers(1, 4))
+    K = int(rng.integers(1, 9))
+    hist, lens = workloads.make_histories(B, L, vocab, seed=case)
+    steps = 6
+    m = rng.integers(0, K + 2, (steps, B)).astype(np.int32)
+    start = np.maximum(lens - m.sum(0), 0).astype(np.int32)
+    cap = _cap(L, n_min, n_max)
+    tables = torch.empty(gpu_lib.ngram_map_bytes(B, cap), dtype=torch.uint8, device="cuda")
+    h = _dev(hist)
+    print(f"[ngram-map] random case {case}: B={B} L={L} vocab={vocab} n={n_min}..{n_max} hits={hits} K={K}",
+          file=sys.stderr, flush=True)
+    old, new = np.zeros(B, np.int32), start
+    for step in range(steps + 1):
+        d, c, st = _update(gpu_lib, tables, cap, h, old, new, n_min, n_max, hits, K)
+        rd, rc = ngram.propose(hist, new, n_min, n_max, hits, K)
+        assert not st.any()
+        np.testing.assert_array_equal(c, rc, err_msg=f"step {step}")
+        np.testing.assert_array_equal(d, rd, err_msg=f"step {step}")
+        if step < steps:
+            nxt = np.minimum(new + m[step], lens).astype(np.int32)
+            rebuild = rng.random(B) < 0.15  # these sequences are rebuilt from scratch next call
+            old = np.where(rebuild, 0, new).astype(np.int32)
+            new = nxt

@@ -130,3 +130,32 @@ def test_chain_tree_equals_the_linear_greedy_entry_point(gpu_lib):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(n_t.cpu().numpy(), n_lin.cpu().numpy())
     np.testing.assert_array_equal(tok_t.cpu().numpy(), tok_lin.cpu().numpy())
+
+
+N_RANDOM_TREES = int(__import__("os").environ.get("SPECV_RANDOM_TREE_CASES", "16"))
+
+
+@pytest.mark.parametrize("case", range(N_RANDOM_TREES))
+def test_random_trees_match_oracle(gpu_lib, case):
+    """Random tree batches (size, depth structure, vocabulary, dtype, share of
+    tokens that match their parent's arg-max) in rounds by depth (the tests'
+    threshold) against the oracle."""
+    rng = np.random.default_rng(8000 + case)
+    B = int(rng.integers(1, 40))
+    N = int(rng.integers(1, 65))
+    V = int(rng.choice([1, 2, 7, 64, 1000, 4097, 32000]))
+    dt = str(rng.choice(["fp32", "bf16"]))
+    pb = float(rng.choice([0.0, 0.3, 0.7, 1.0]))
+    tb = workloads.make_tree_batch(B, N, V, dt, seed=case, p_branch=pb)
+    match = float(rng.choice([0.0, 0.5, 0.9, 1.0]))
+    amax = np.argmax(workloads.storage_to_f64(tb.logits, dt), axis=2)
+    for b in range(B):
+        for v in range(1, N):
+            if rng.random() < match:
+                tb.tokens[b, v] = amax[b, tb.parents[b, v]]
+    say(f"[tree] random case {case}: B={B} N={N} V={V} {dt} p_branch={pb} match={match}")
+    rt, rp, rn = tree.verify_tree_greedy(tb.logits, tb.tokens, tb.parents, tb.dtype)
+    tok, path, n = _run_tree(gpu_lib, tb)
+    np.testing.assert_array_equal(n, rn)
+    np.testing.assert_array_equal(tok, rt)
+    np.testing.assert_array_equal(path, rp)
