@@ -64,9 +64,8 @@ typedef enum { SPECV_F32 = 0, SPECV_BF16 = 1 } specv_dtype_t;
  * draw to the fp64 path, so in principle this bit may differ between two
  * identical calls.  The tokens, the counts and the other bits never do (the
  * fp64 path draws the same token wherever the fast one is certified).  Rows
- * of at most 2048 tokens in batches of at most eight sequences per compute
- * unit take one launch that draws every token in fp64: there the bit is set
- * on every sequence. */
+ * of at most 2048 tokens take one launch that draws every token in fp64
+ * (see spec_short_max_seqs): there the bit is set on every sequence. */
 #define SPECV_FLAG_FP64      1  /* the draw was made by the fp64 path: the fp32 draw could not certify its token */
 #define SPECV_FLAG_ZW_ZERO   2  /* residual mass was zero after rounding; drew from p_n instead */
 #define SPECV_FLAG_BAD_DRAFT 4  /* an evaluated draft id was outside [0, V) and was rejected */
@@ -298,6 +297,21 @@ int spec_ngram_propose(const int32_t* history, const int32_t* lengths, int B, in
  * returns it.  Both ways give the same outputs.
  */
 double spec_rounds_min_bytes(double bytes);
+
+/*
+ * spec_short_max_seqs - the largest batch whose sampling calls on rows of at
+ * most 2048 tokens take the one-launch path (one workgroup per sequence does
+ * every step: normalisers, acceptance test of u_k < min(1, p_k(x_k) /
+ * q_k(x_k)) ([B] "验收标准的精确数学") and the residual or bonus draw in fp64
+ * ([B] "拒绝之后怎么办？——残差分布")); larger batches take the general path
+ * (row sweep, per-sequence fast draw, fp64 draw for what it cannot
+ * certify).  The default is no limit (INT_MAX), or SPECV_SHORT_MAX_SEQS from
+ * the environment at the first use.  n >= 0 sets the limit for the process
+ * (0: the general path always) and returns the previous one; a negative value
+ * only returns it.  Both paths give the same tokens and counts; the flags
+ * differ in SPECV_FLAG_FP64 (see there).
+ */
+int spec_short_max_seqs(int n);
 
 /*
  * The n-gram map: spec_ngram_propose's proposals kept up to date in a hash

@@ -33,7 +33,7 @@ EXPORTS = ("spec_verify_workspace_size", "spec_verify", "spec_verify_noalloc", "
            "spec_verify_sweep_timed",
            "spec_verify_ragged",
            "spec_verify_ragged_ex", "spec_verify_tree_workspace_size", "spec_verify_tree_greedy", "spec_tree_mask", "spec_ngram_propose",
-           "spec_ngram_map_bytes", "spec_ngram_map_update", "spec_rounds_min_bytes",
+           "spec_ngram_map_bytes", "spec_ngram_map_update", "spec_rounds_min_bytes", "spec_short_max_seqs",
            "spec_debug_enable", "spec_debug_counters", "spec_debug_reset",
            "spec_verify_strerror", "spec_verify_version")
 
@@ -85,6 +85,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spec_ngram_propose.restype = i32
     lib.spec_rounds_min_bytes.argtypes = [ctypes.c_double]
     lib.spec_rounds_min_bytes.restype = ctypes.c_double
+    lib.spec_short_max_seqs.argtypes = [ctypes.c_int]
+    lib.spec_short_max_seqs.restype = ctypes.c_int
     lib.spec_ngram_map_bytes.argtypes = [i32, i32]
     lib.spec_ngram_map_bytes.restype = sz
     lib.spec_ngram_map_update.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -454,3 +456,10 @@ def rounds_min_bytes(bytes_: Optional[float] = None) -> float:
     """The input size from which verify calls read rows in rounds (early
     exit); sets it when bytes_ is given.  Returns the previous value."""
     return float(load().spec_rounds_min_bytes(-1.0 if bytes_ is None else float(bytes_)))
+
+
+def short_max_seqs(n: Optional[int] = None) -> int:
+    """The largest batch whose sampling calls on rows of at most 2048 tokens
+    take the one-launch path; sets it when n is given (0: never).  Returns the
+    previous value."""
+    return int(load().spec_short_max_seqs(-1 if n is None else int(n)))

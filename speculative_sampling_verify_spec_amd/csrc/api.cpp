@@ -3,6 +3,7 @@
 // or keeps state between calls.
 #include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -168,22 +169,24 @@ std::atomic<double>& rounds_threshold() {
 
 double rounds_min_bytes() { return rounds_threshold().load(std::memory_order_relaxed); }
 
-// Largest batch that takes the one-launch path for short rows (k_short):
-// kShortSeqsPerCU sequences per CU, or SPECV_SHORT_MAX_SEQS from the
-// environment (read once per process; 0 turns the path off).
-int short_max_seqs() {
-  static std::once_flag once;
-  static long v = -1;
-  std::call_once(once, [] {
+// Largest batch that takes the one-launch path for short rows (k_short): no
+// limit, or SPECV_SHORT_MAX_SEQS from the environment (read at the first
+// use), or what spec_short_max_seqs set (0 turns the path off).
+std::atomic<int>& short_limit() {
+  static std::atomic<int> v{[] {
+    int t = INT_MAX;
     const char* e = std::getenv("SPECV_SHORT_MAX_SEQS");
     if (e && *e) {
       char* end = nullptr;
       const long d = std::strtol(e, &end, 10);
-      if (end != e && d >= 0) v = d;
+      if (end != e && d >= 0) t = static_cast<int>(std::min(d, static_cast<long>(INT_MAX)));
     }
-  });
-  return v >= 0 ? static_cast<int>(std::min(v, 1L << 30)) : kShortSeqsPerCU * device_cus();
+    return t;
+  }()};
+  return v;
 }
+
+int short_max_seqs() { return short_limit().load(std::memory_order_relaxed); }
 
 // The first level of the last round for K drafts.
 int last_round_begin(int K) {
@@ -606,6 +609,11 @@ int spec_tree_mask(const int32_t* parents, int B, int N, uint8_t* out_mask, int3
 double spec_rounds_min_bytes(double bytes) {
   std::atomic<double>& t = sv::rounds_threshold();
   return bytes >= 0.0 && std::isfinite(bytes) ? t.exchange(bytes) : t.load();
+}
+
+int spec_short_max_seqs(int n) {
+  std::atomic<int>& t = sv::short_limit();
+  return n >= 0 ? t.exchange(n) : t.load();
 }
 
 int spec_debug_enable(int on) { return sv::debug_enabled_flag(&on) ? 1 : 0; }

@@ -18,7 +18,7 @@
 //    acceptance test needs no gather.
 //  - Acceptance.  Wave 0 tests u_k < min(1, p_k(x_k) / q_k(x_k)) as an fp64
 //    log2 ratio per draft; a ballot gives n, the first rejection.
-//  - Draw.  In fp64 over the whole workgroup, four tokens per thread in token
+//  - Draw.  In fp64 over the whole workgroup, CAP / 512 tokens per thread in token
 //    order.  P = exp(x / T - L'p) and Q = exp(y / T - L'q) from the decisive
 //    row(s), normalised by their own sums: w = max(0, P - rho Q) with
 //    rho = sum P / sum Q (w = P for a bonus draw, and when the residual sums
@@ -43,18 +43,20 @@ namespace {
 
 constexpr int kSBlock = 512;  // threads per workgroup (8 waves: up to 256 registers each)
 constexpr int kSWaves = kSBlock / kWave;
-constexpr int kSTok = kShortMaxV / kSBlock;  // draw tokens per thread
 constexpr int kSRowsMax = 2 * SPECV_MAX_K + 1;
-static_assert(kShortMaxV % kSBlock == 0, "whole draw tokens per thread");
+// Rows are held for a capacity CAP of tokens: kShortMaxV, or half of it for
+// rows that fit (half the loads, exps and draw tokens per lane).
+constexpr int kSCapSmall = kShortMaxV / 2;
+static_assert(kSCapSmall % kSBlock == 0, "whole draw tokens per thread");
 
 // One row's elements as a lane holds them: units lane, lane + 64, ...
 // (16-byte vectors on the vector path, single elements otherwise), at most
-// NU per lane for a row of kShortMaxV tokens.  Loads are branch-free: an
-// index past the row reads the row's last unit again and is masked to -inf.
-template <int DT, bool VEC>
+// NU per lane for a row of CAP tokens.  Loads are branch-free: an index past
+// the row reads the row's last unit again and is masked to -inf.
+template <int DT, bool VEC, int CAP>
 struct ShortRow {
   static constexpr int PV = VEC ? Elt<DT>::kPerVec : 1;
-  static constexpr int NU = kShortMaxV / PV / kWave;
+  static constexpr int NU = CAP / PV / kWave;
   uint4 raw[VEC ? NU : 1];
   float el[VEC ? 1 : NU];
 
@@ -119,9 +121,10 @@ __device__ inline const void* short_row_ptr(const Params& p, long s, int i) {
   return i <= p.K ? row_ptr<DT>(p.lp, s * (p.K + 1) + i, p.V) : row_ptr<DT>(p.lq, s * p.K + (i - p.K - 1), p.V);
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int CAP>
 __global__ __launch_bounds__(kSBlock) void k_short(Params p) {
-  using Row = ShortRow<DT, VEC>;
+  using Row = ShortRow<DT, VEC, CAP>;
+  constexpr int kSTok = CAP / kSBlock;  // draw tokens per thread
   const long s = p.seq0 + blockIdx.x;
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int K = p.K, nrows = 2 * K + 1;
@@ -292,11 +295,17 @@ __global__ __launch_bounds__(kSBlock) void k_short(Params p) {
   }
 }
 
+template <int DT, bool VEC, int CAP>
+void launch_short_cap(const Params& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  const dim3 grid(static_cast<unsigned>(p.nseq)), block(kSBlock);
+  if (e0 || e1) hipExtLaunchKernelGGL((k_short<DT, VEC, CAP>), grid, block, 0, st, e0, e1, 0, p);
+  else hipLaunchKernelGGL((k_short<DT, VEC, CAP>), grid, block, 0, st, p);
+}
+
 template <int DT, bool VEC>
 void launch_short_t(const Params& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-  const dim3 grid(static_cast<unsigned>(p.nseq)), block(kSBlock);
-  if (e0 || e1) hipExtLaunchKernelGGL((k_short<DT, VEC>), grid, block, 0, st, e0, e1, 0, p);
-  else hipLaunchKernelGGL((k_short<DT, VEC>), grid, block, 0, st, p);
+  if (p.V <= kSCapSmall) launch_short_cap<DT, VEC, kSCapSmall>(p, st, e0, e1);
+  else launch_short_cap<DT, VEC, kShortMaxV>(p, st, e0, e1);
 }
 
 }  // namespace

@@ -14,13 +14,13 @@ constexpr int kMaxDrawChunks = 256;   // fp64 draw chunks per row: one wave comb
 constexpr int kXBlock = 128;          // threads that compute one fp64 draw chunk's sums
 constexpr int kSoloMaxChunks = 2;     // rows of at most this many fp64 draw chunks: one fp64 launch (k_exact_solo)
 constexpr int kEagerMaxRounds = 4;    // k_verify's chunk-sum workgroups: at most this many chunks per group of 128 threads
-// Rows of at most kShortMaxV tokens (two fp64 draw chunks of 1024) in batches
-// of at most kShortSeqsPerCU sequences per CU (or SPECV_SHORT_MAX_SEQS) take
-// one launch for the whole step in sampling mode (k_short).  Measured at
-// K = 4, V = 1000 fp32 (us per call, one launch against the general path):
-// B = 1 8.2 / 11.4, B = 256 9.2 / 22.7, B = 2048 58.2 / 65.2.
+// Rows of at most kShortMaxV tokens (two fp64 draw chunks of 1024) take one
+// launch for the whole step in sampling mode (k_short), at any batch size
+// unless spec_short_max_seqs limits it.  Measured (us per call, one launch
+// against the general path): K = 4, V = 1000 fp32: B = 1 6.1 / 11.4,
+// B = 256 7.5 / 22.7, B = 4096 60.2 / 174.6, B = 16384 227 / 508; V = 2000
+// fp32, B = 8192: 251 / 298; K = 5, V = 2048 bf16, B = 8192: 234 / 402.
 constexpr int kShortMaxV = kSoloMaxChunks * 1024;
-constexpr int kShortSeqsPerCU = 8;
 
 // Elements one lane of a row sweep holds: 16-byte units on the vector path,
 // sixteen single elements on the scalar path.  The vector path has two

@@ -23,6 +23,7 @@ sigs = {
     "spec_ngram_propose": ([vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp], i32),
     "spec_ngram_map_bytes": ([i32, i32], sz),
     "spec_rounds_min_bytes": ([ctypes.c_double], ctypes.c_double),
+    "spec_short_max_seqs": ([ctypes.c_int], ctypes.c_int),
     "spec_ngram_map_update": ([vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp], i32),
     "spec_verify_strerror": ([i32], ctypes.c_char_p),
     "spec_verify_version": ([], ctypes.c_char_p),
@@ -95,6 +96,8 @@ assert lib.spec_ngram_map_bytes(4, 1024) == 4 * (16 + 16 * 1024) and lib.spec_ng
 old = lib.spec_rounds_min_bytes(-1.0)
 assert lib.spec_rounds_min_bytes(12345.0) == old and lib.spec_rounds_min_bytes(float("nan")) == 12345.0
 assert lib.spec_rounds_min_bytes(old) == 12345.0
+old = lib.spec_short_max_seqs(-1)
+assert lib.spec_short_max_seqs(5) == old and lib.spec_short_max_seqs(-1) == 5 and lib.spec_short_max_seqs(old) == 5
 assert lib.spec_ngram_map_update(WS, 1024, L, TT, PA, 4, 100, 3, 2, 1, 5, OTT, OP, None, None) == -2
 assert lib.spec_ngram_map_update(WS + 8, 1024, L, TT, PA, 4, 100, 1, 4, 1, 5, OTT, OP, None, None) == -6
 assert lib.spec_ngram_map_update(WS, 1024, L, TT, PA, 4, 100, 1, 4, 1, 5, OTT, OP, None, None) == -7

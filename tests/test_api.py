@@ -209,6 +209,17 @@ def test_rounds_threshold_knob(lib):
     assert lib.spec_rounds_min_bytes(-1.0) == old
 
 
+def test_short_path_limit_knob(lib):
+    old = lib.spec_short_max_seqs(-1)
+    try:
+        assert lib.spec_short_max_seqs(77) == old
+        assert lib.spec_short_max_seqs(-3) == 77 and lib.spec_short_max_seqs(0) == 77
+        assert lib.spec_short_max_seqs(-1) == 0
+    finally:
+        lib.spec_short_max_seqs(old)
+    assert lib.spec_short_max_seqs(-1) == old
+
+
 def test_noalloc_entry_point_checks(lib):
     """spec_verify_noalloc runs spec_verify's host-side checks, and rejects a
     shape whose workspace exceeds its static scratch before any HIP call."""
