@@ -35,7 +35,7 @@ namespace sv {
 
 namespace {
 
-constexpr unsigned kExactSeqs = 32;              // queued sequences the kernels cover per pass
+constexpr unsigned kExactSeqs = 32;              // queued sequences the kernels cover per pass, at least
 constexpr unsigned kSoloSeqs = 256;              // queued sequences k_exact_solo covers per pass
 constexpr int kMaxPer = (kMaxDrawChunks + kWave - 1) / kWave;  // chunks per lane in the select
 
@@ -407,9 +407,15 @@ void launch_all(const Params& p, hipStream_t st) {
     hipLaunchKernelGGL((k_exact_solo<DT, VEC>), dim3(ns < kSoloSeqs ? ns : kSoloSeqs), block, 0, st, p);
     return;
   }
-  // grids cover up to kExactSeqs queued sequences in one pass; idle
-  // workgroups exit at once
-  const unsigned nx = ns < kExactSeqs ? ns : kExactSeqs;
+  // grids cover up to max(kExactSeqs, B / 4) queued sequences in one pass
+  // (more are walked in passes); idle workgroups exit at once.  Sequences
+  // whose residuals are flat queue a fifth of their draws or more: a B / 4
+  // grid measured 161.2 -> 128.6 us per call at B = 1024 (K = 5, V = 32000,
+  // bf16) and 333.1 -> 263.7 at B = 2048 against a 32-sequence grid, with B =
+  // 1024 of the T = 0.7, V = 128256 recipe unchanged (463.0 -> 454.7) and
+  // B = 256 (64 slots instead of 32) within noise.
+  const unsigned cover = ns / 4 > kExactSeqs ? ns / 4 : kExactSeqs;
+  const unsigned nx = ns < cover ? ns : cover;
   hipLaunchKernelGGL((k_exact_chunks<DT, VEC>), dim3(nx * p.R3), block, 0, st, p);
   hipLaunchKernelGGL((k_exact_select<DT, VEC>), dim3(nx), block, 0, st, p);
 }

@@ -89,7 +89,8 @@ def test_sums_ahead_match_the_queued_path(gpu_lib, cfg, V):
     run both fp64 kernels.  The same 64 sequences, with edge uniforms that
     send many of them to the fp64 draw, drawn both ways (alone, and among
     320) give the same tokens, counts and flags bit for bit, and the
-    oracle's."""
+    oracle's.  Nearly all of the 320 are queued, more than the fp64 grids
+    cover in one pass (80), so the kernels also walk the queue in passes."""
     b = workloads.make_batch(cfg, seqs=range(320), workers=workloads.default_workers(), V=V)
     ref = oracle.verify_batch(b, workers=workloads.default_workers())
     ur, chosen, _ = edge_uniforms(b, ref)
