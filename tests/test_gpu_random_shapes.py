@@ -91,3 +91,36 @@ def test_random_split_workload_matches_oracle(gpu_lib, case):
     print(f"[random-split] case {case}: {b.wl.describe()}{' ragged' if ragged else ''}", file=sys.stderr,
           flush=True)
     compare(b, run_gpu(gpu_lib, b), oracle.verify_batch(b)).check()
+
+
+# Large batches of short rows (at most 2048 tokens): the one-launch path at
+# any batch size, on both capacities (rows of at most 1024 tokens, and up to
+# 2048), against the oracle on every sequence.
+N_SHORT_CASES = int(os.environ.get("SPECV_RANDOM_SHORT_CASES", "6"))
+SHORT_VOCABS = [2, 63, 257, 1000, 1023, 1024, 1025, 1500, 2047, 2048]
+
+
+def random_short_batch(case: int):
+    rng = np.random.default_rng(13000 + case)
+    B = int(rng.integers(300, 4000))
+    K = int(rng.integers(1, 9))
+    V = int(rng.choice(SHORT_VOCABS))
+    dt = str(rng.choice(["fp32", "bf16"]))
+    T = float(np.float32(rng.choice([0.3, 0.7, 1.0, 1.7])))
+    wl = workloads.Workload(f"random-short-{case}", B, K, V, dt, T, float(rng.choice([0.5, 2.0])),
+                            float(rng.choice([0.0, 1.1, 3.3])), "noise", float(rng.choice([0.1, 0.8, 2.0])))
+    b = workloads.make_batch(1, wl=wl, seed=case, workers=workloads.default_workers())
+    if rng.random() < 0.3:
+        b = dataclasses.replace(b, num_drafts=workloads.ragged_draft_counts(B, K, seed=case, low=0))
+    return b
+
+
+@pytest.mark.parametrize("case", range(N_SHORT_CASES))
+def test_random_large_batch_of_short_rows_matches_oracle(gpu_lib, case):
+    b = random_short_batch(case)
+    ragged = getattr(b, "num_drafts", None) is not None
+    print(f"[random-short] case {case}: {b.wl.describe()}{' ragged' if ragged else ''}", file=sys.stderr,
+          flush=True)
+    out = run_gpu(gpu_lib, b)
+    assert np.all(out.flags & gpu_lib.FLAG_FP64), "short rows: every draw is an fp64 draw (one-launch path)"
+    compare(b, out, oracle.verify_batch(b, workers=workloads.default_workers())).check()
