@@ -36,6 +36,7 @@ namespace sv {
 namespace {
 
 constexpr unsigned kExactSeqs = 32;              // queued sequences the kernels cover per pass, at least
+constexpr unsigned kExactMaxGroups = 8192;       // chunk workgroups per pass, at most (beyond kExactSeqs rows)
 constexpr unsigned kSoloSeqs = 256;              // queued sequences k_exact_solo covers per pass
 constexpr int kMaxPer = (kMaxDrawChunks + kWave - 1) / kWave;  // chunks per lane in the select
 
@@ -407,14 +408,18 @@ void launch_all(const Params& p, hipStream_t st) {
     hipLaunchKernelGGL((k_exact_solo<DT, VEC>), dim3(ns < kSoloSeqs ? ns : kSoloSeqs), block, 0, st, p);
     return;
   }
-  // grids cover up to max(kExactSeqs, B / 4) queued sequences in one pass
-  // (more are walked in passes); idle workgroups exit at once.  Sequences
-  // whose residuals are flat queue a fifth of their draws or more: a B / 4
-  // grid measured 161.2 -> 128.6 us per call at B = 1024 (K = 5, V = 32000,
-  // bf16) and 333.1 -> 263.7 at B = 2048 against a 32-sequence grid, with B =
-  // 1024 of the T = 0.7, V = 128256 recipe unchanged (463.0 -> 454.7) and
-  // B = 256 (64 slots instead of 32) within noise.
-  const unsigned cover = ns / 4 > kExactSeqs ? ns / 4 : kExactSeqs;
+  // grids cover up to max(kExactSeqs, min(B / 4, kExactMaxGroups / chunks))
+  // queued sequences in one pass (more are walked in passes); idle
+  // workgroups exit at once, but each still costs a dispatch and a load.
+  // Sequences whose residuals are flat queue a fifth of their draws or more:
+  // against a 32-sequence grid, a B / 4 grid measured 161.2 -> 128.6 us per
+  // call at B = 1024 (K = 5, V = 32000, bf16) and 333.1 -> 263.7 at B = 2048,
+  // B = 1024 of the T = 0.7, V = 128256 recipe 463.0 -> 454.7, B = 256
+  // within noise; the cap on workgroups keeps a batch that queues nothing
+  // (B = 1024, V = 256000, fp32: 250 chunks a row) at its 32-sequence grid.
+  const unsigned cap = kExactMaxGroups / static_cast<unsigned>(p.R3);
+  const unsigned want = ns / 4 < cap ? ns / 4 : cap;
+  const unsigned cover = want > kExactSeqs ? want : kExactSeqs;
   const unsigned nx = ns < cover ? ns : cover;
   hipLaunchKernelGGL((k_exact_chunks<DT, VEC>), dim3(nx * p.R3), block, 0, st, p);
   hipLaunchKernelGGL((k_exact_select<DT, VEC>), dim3(nx), block, 0, st, p);
