@@ -308,8 +308,10 @@ double spec_rounds_min_bytes(double bytes);
  * certify).  The default is no limit (INT_MAX), or SPECV_SHORT_MAX_SEQS from
  * the environment at the first use.  n >= 0 sets the limit for the process
  * (0: the general path always) and returns the previous one; a negative value
- * only returns it.  Both paths give the same tokens and counts; the flags
- * differ in SPECV_FLAG_FP64 (see there).
+ * only returns it.  Both paths compute the same method; their fp32
+ * normalisers round differently, so a count (and then the token) can differ
+ * only where an acceptance test is a near-tie, and SPECV_FLAG_FP64 differs
+ * (see there).  Thread-safe; a call already under way keeps the path it took.
  */
 int spec_short_max_seqs(int n);
 
