@@ -1,6 +1,9 @@
 // Host side of libspecverify: argument checks, workspace layout and the
-// launch sequence of one verify step.  Nothing here allocates, synchronises
-// or keeps state between calls.
+// launch sequence of one verify step.  Nothing here allocates, and nothing
+// synchronises but the debug counters' read and reset.  State kept between
+// calls: per device, the CU count and the static scratch's address (each
+// looked up once) and the debug counters; per process, the two path
+// thresholds (spec_rounds_min_bytes, spec_short_max_seqs).
 #include <algorithm>
 #include <atomic>
 #include <climits>
@@ -105,9 +108,7 @@ Layout make_layout(int B, int K, int V, int dtype, bool vec, bool greedy, bool t
 
 namespace {
 
-// Compute units of the current device, queried once per device (0 when the
-// device cannot be queried).
-constexpr int kMaxDevices = 64;
+constexpr int kMaxDevices = 64;  // devices the per-device lookups below cover
 
 // Device address of `scratch` on the current device, looked up once per
 // device with that device current; null if the lookup fails.
@@ -123,6 +124,8 @@ void* scratch_ptr() {
   return ptr[dev];
 }
 
+// Compute units of the current device, queried once per device (0 when the
+// device cannot be queried).
 int device_cus() {
   static std::once_flag once[kMaxDevices];
   static int cus[kMaxDevices];
