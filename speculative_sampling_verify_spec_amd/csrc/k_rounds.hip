@@ -66,7 +66,7 @@ template <int DT, bool GREEDY>
 __global__ __launch_bounds__(kBlock) void k_round_accept(Params p) {
   const int lane = threadIdx.x % kWave;
   // the wave's sequence, in scalar registers (its count and kbs are scalar loads)
-  const long local = static_cast<long>(blockIdx.x) * kWaves +
+  const long local = static_cast<long>(blockIdx.x) * (blockDim.x / kWave) +
                      __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
   if (local >= p.nseq) return;  // uniform over the wave
   const long s = p.seq0 + local;
@@ -145,7 +145,10 @@ __global__ __launch_bounds__(kBlock) void k_round_accept(Params p) {
 }  // namespace
 
 hipError_t launch_round_accept(const Params& p, int dtype, bool greedy, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((p.nseq + kWaves - 1) / kWaves)), block(kBlock);
+  // one wave per workgroup, spread over the CUs (interleaved A/B against four
+  // sequences per 256-thread workgroup, us per step: headline 138.75 ->
+  // 138.62, greedy 81.00 -> 80.72, headline at B = 96 76.10 -> 75.80)
+  const dim3 grid(static_cast<unsigned>(p.nseq)), block(kWave);
   if (greedy) hipLaunchKernelGGL((k_round_accept<0, true>), grid, block, 0, st, p);
   else if (dtype == 1) hipLaunchKernelGGL((k_round_accept<1, false>), grid, block, 0, st, p);
   else hipLaunchKernelGGL((k_round_accept<0, false>), grid, block, 0, st, p);
